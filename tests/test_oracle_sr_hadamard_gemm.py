@@ -1,0 +1,345 @@
+"""Pins of the oracle's stochastic rounding, Philox, Hadamard-32, tensor
+layouts, dequantize and fp64 dot product (CPU only)."""
+import math
+import os
+import shutil
+import subprocess
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from mx_brute import FMT_BITS, Grid, brute_block
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+# --------------------------------------------------------------------------
+# Philox4x32-10 against rocRAND's generator, compiled here as host code
+# --------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def rocrand_ref(tmp_path_factory):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available to build the rocRAND host reference")
+    exe = str(tmp_path_factory.mktemp("rr") / "rr")
+    src = os.path.join(HERE, "helpers", "rocrand_philox_ref.cpp")
+    r = subprocess.run([hipcc, "-O1", src, "-o", exe], capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.skip("could not build rocRAND host reference: " + r.stderr[-300:])
+
+    def words(seed, sub, off, count):
+        out = subprocess.run([exe, str(seed), str(sub), str(off), str(count)],
+                             capture_output=True, text=True, check=True).stdout.split()
+        return [int(w) for w in out]
+    return words
+
+
+def test_philox_matches_rocrand(oracle, rocrand_ref):
+    for seed in (0, 42, 0x123456789ABCDEF0, 0xFFFFFFFFFFFFFFFF):
+        for sub in (0, 1):
+            ref = rocrand_ref(seed, sub, 0, 64)
+            mine = []
+            for j in range(16):
+                mine += [int(w) for w in oracle.philox4x32_10(
+                    [j, 0, sub, 0], [seed & 0xFFFFFFFF, seed >> 32])]
+            assert mine == ref
+
+
+def test_sr_word_mapping_matches_rocrand_stream(oracle, rocrand_ref):
+    """Element i's word is word i of the stream (seed, subsequence = layout)
+    started 4*counter_offset words in."""
+    for seed, off, layout in [(42, 0, 0), (42, 0, 1), (7, 1000, 0), (2 ** 40 + 3, 5, 1)]:
+        ref = rocrand_ref(seed, layout, 4 * off, 40)
+        mine = [oracle.sr_word(seed, off, layout, i) for i in range(40)]
+        assert mine == ref
+
+
+# --------------------------------------------------------------------------
+# stochastic rounding
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("fmt", range(6))
+def test_sr_matches_brute_force(oracle, fmt):
+    grid = Grid(oracle, fmt)
+    rng = np.random.default_rng(400 + fmt)
+    for t in range(120):
+        v = (rng.standard_normal(32) * 2.0 ** rng.uniform(-30, 30)).astype(np.float32)
+        r = rng.integers(0, 2 ** 32, size=32, dtype=np.uint64).astype(np.uint32)
+        if t % 4 == 0:
+            r[:] = 0
+        elif t % 4 == 1:
+            r[:] = 0xFFFFFFFF
+        sc, q = oracle.quantize_block(fmt, v, oracle.SR, r)
+        bsc, bq = brute_block(grid, v, rnd=r)
+        assert sc == bsc and list(q) == bq
+
+
+def test_sr_threshold_and_unbiased(oracle):
+    """Round up happens exactly for r < floor(frac * 2^32); averaged over
+    uniform words the result is unbiased."""
+    o = oracle
+    v = np.zeros(32, np.float32)
+    v[0] = np.float32(448.0)
+    v[1] = np.float32(1.3)  # E4M3: neighbours 1.25 and 1.375, frac = 0.4
+    frac = (Fraction(float(v[1])) - Fraction(5, 4)) / Fraction(1, 8)
+    F = math.floor(frac * 2 ** 32)
+    r = np.zeros(32, np.uint32)
+    r[1] = F - 1
+    assert o.elem_value(o.E4M3, int(o.quantize_block(o.E4M3, v, o.SR, r)[1][1])) == 1.375
+    r[1] = F
+    assert o.elem_value(o.E4M3, int(o.quantize_block(o.E4M3, v, o.SR, r)[1][1])) == 1.25
+    rng = np.random.default_rng(5)
+    for fmt, val in [(o.E2M1, 0.3), (o.E4M3, -3.3), (o.INT8, 0.01), (o.E3M2, 0.07)]:
+        v = np.zeros(32, np.float32)
+        v[0] = np.float32(o.elem_maxnorm(fmt))
+        v[1:] = np.float32(val)
+        n = 4000
+        acc = 0.0
+        for _ in range(n // 31 + 1):
+            r = rng.integers(0, 2 ** 32, size=32, dtype=np.uint64).astype(np.uint32)
+            sc, q = o.quantize_block(fmt, v, o.SR, r)
+            acc += sum(o.elem_value(fmt, int(c)) for c in q[1:]) * 2.0 ** (sc - 127)
+        cnt = 31 * (n // 31 + 1)
+        mean = acc / cnt
+        grid = Grid(o, fmt)
+        lo = max(x for x in grid.values if x <= abs(Fraction(float(np.float32(val)))))
+        hi = min(x for x in grid.values if x >= abs(Fraction(float(np.float32(val)))))
+        sigma = float(hi - lo) / 2 / math.sqrt(cnt)
+        assert abs(mean - float(np.float32(val))) <= 4 * sigma + 1e-12
+
+
+# --------------------------------------------------------------------------
+# Hadamard-32
+# --------------------------------------------------------------------------
+def sylvester32():
+    h = np.array([[1.0]])
+    for _ in range(5):
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+C32 = np.float32(1.0 / math.sqrt(32.0))
+
+
+def test_hadamard_matrix_identities(oracle):
+    H = sylvester32()
+    np.testing.assert_array_equal(H @ H.T, 32 * np.eye(32))
+    assert np.float32(np.array([0x3E3504F3], np.uint32).view(np.float32)[0]) == C32
+    for j in range(32):
+        e = np.zeros(32, np.float32)
+        e[j] = 1.0
+        np.testing.assert_array_equal(oracle.hadamard32(e), (H[:, j] * C32).astype(np.float32))
+
+
+def test_hadamard_integer_inputs_exact(oracle):
+    """Integer inputs below 2^18: every butterfly sum is exact, so the result
+    equals the fp64 Sylvester product followed by one fp32 multiply."""
+    H = sylvester32()
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        x = rng.integers(-(2 ** 18), 2 ** 18, 32).astype(np.float32)
+        signs = int(rng.integers(0, 2 ** 32))
+        d = np.array([-1.0 if (signs >> j) & 1 else 1.0 for j in range(32)])
+        ref = (H @ (d * x.astype(np.float64))).astype(np.float32) * C32
+        np.testing.assert_array_equal(oracle.hadamard32(x, signs), ref)
+
+
+def test_hadamard_general_error_bound(oracle):
+    H = sylvester32()
+    rng = np.random.default_rng(8)
+    for _ in range(200):
+        x = (rng.standard_normal(32) * 2.0 ** rng.uniform(-20, 20)).astype(np.float32)
+        ref = H @ x.astype(np.float64) * (1 / math.sqrt(32))
+        got = oracle.hadamard32(x).astype(np.float64)
+        bound = 7 * 2.0 ** -24 * np.abs(x).astype(np.float64).sum() / math.sqrt(32)
+        assert np.all(np.abs(got - ref) <= bound)
+
+
+# --------------------------------------------------------------------------
+# tensor layouts and packing
+# --------------------------------------------------------------------------
+def unpack(q_row_bytes, fmt, cols):
+    """Element codes of one packed row, from the documented bit layout."""
+    bits = FMT_BITS[fmt]
+    if bits == 8:
+        return list(q_row_bytes[:cols])
+    big = int.from_bytes(bytes(q_row_bytes), "little")
+    if bits == 4:
+        return [(big >> (4 * j)) & 0xF for j in range(cols)]
+    out = []
+    for j in range(cols):
+        blk = int.from_bytes(bytes(q_row_bytes[(j // 32) * 24:(j // 32) * 24 + 24]), "little")
+        out.append((blk >> (6 * (j % 32))) & 0x3F)
+    return out
+
+
+@pytest.mark.parametrize("fmt", range(6))
+def test_row_layout_is_blockwise(oracle, fmt):
+    rng = np.random.default_rng(9 + fmt)
+    x = (rng.standard_normal((5, 96)) * np.exp2(rng.uniform(-8, 8, (5, 1)))).astype(np.float32)
+    out = oracle.quantize(x, fmt, oracle.LAYOUT_ROW)
+    assert out["q_row"].shape == (5, 96 * FMT_BITS[fmt] // 8)
+    for r in range(5):
+        codes = unpack(out["q_row"][r], fmt, 96)
+        for b in range(3):
+            sc, q = oracle.quantize_block(fmt, x[r, 32 * b:32 * b + 32])
+            assert out["s_row"][r, b] == sc
+            assert codes[32 * b:32 * b + 32] == list(q)
+
+
+@pytest.mark.parametrize("fmt", [0, 2, 4, 5])
+def test_colt_equals_row_of_transpose(oracle, fmt):
+    """Column blocks stored transposed are the row blocks of X^T (RNE)."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((64, 96)).astype(np.float32)
+    a = oracle.quantize(x, fmt, oracle.LAYOUT_COLT)
+    b = oracle.quantize(np.ascontiguousarray(x.T), fmt, oracle.LAYOUT_ROW)
+    np.testing.assert_array_equal(a["q_colt"], b["q_row"])
+    np.testing.assert_array_equal(a["s_colt"], b["s_row"])
+    # and the two axes really differ (conversion does not commute with transpose)
+    c = oracle.quantize(x, fmt, oracle.LAYOUT_ROW)
+    deq_row = oracle.dequantize(c["q_row"], c["s_row"], fmt, 64, 96)
+    deq_col = oracle.dequantize(a["q_colt"], a["s_colt"], fmt, 96, 64).T
+    assert not np.array_equal(deq_row, deq_col)
+
+
+def test_bf16_source_equals_widened_fp32(oracle):
+    from microscaling_block_scaled_amd.synth import bf16_bits, bf16_to_f32
+    rng = np.random.default_rng(12)
+    b = bf16_bits(rng.standard_normal((32, 64)).astype(np.float32))
+    b[0, :5] = [1, 0x8001, 0x7F, 0, 0x8000]  # bf16 subnormals and zeros
+    x = bf16_to_f32(b)
+    for lay in (1, 2, 3):
+        p = oracle.quantize(b, 0, lay)
+        q = oracle.quantize(x, 0, lay)
+        for k in p:
+            np.testing.assert_array_equal(p[k], q[k])
+
+
+def test_sr_tensor_uses_logical_index_words(oracle):
+    """Row-wise SR of element (r, c) uses word r*cols+c of layout 0; col-wise
+    uses the same index with layout 1."""
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((32, 64)).astype(np.float32)
+    seed, off = 42, 17
+    out = oracle.quantize(x, oracle.E2M1, 3, oracle.SR, seed=seed, counter_offset=off)
+    for r in (0, 5, 31):
+        for b in range(2):
+            words = [oracle.sr_word(seed, off, 0, r * 64 + 32 * b + k) for k in range(32)]
+            sc, q = oracle.quantize_block(oracle.E2M1, x[r, 32 * b:32 * b + 32], oracle.SR, words)
+            assert out["s_row"][r, b] == sc
+            assert unpack(out["q_row"][r], oracle.E2M1, 64)[32 * b:32 * b + 32] == list(q)
+    for c in (0, 33, 63):
+        words = [oracle.sr_word(seed, off, 1, k * 64 + c) for k in range(32)]
+        sc, q = oracle.quantize_block(oracle.E2M1, x[:, c], oracle.SR, words)
+        assert out["s_colt"][c, 0] == sc
+        assert unpack(out["q_colt"][c], oracle.E2M1, 32) == list(q)
+
+
+def test_hadamard_tensor_applies_per_block(oracle):
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((32, 64)).astype(np.float32)
+    signs = 0x8421_1248
+    out = oracle.quantize(x, oracle.E4M3, 3, flags=oracle.FLAG_HADAMARD32, hadamard_signs=signs)
+    for r in (0, 31):
+        hx = oracle.hadamard32(x[r, 32:64], signs)
+        sc, q = oracle.quantize_block(oracle.E4M3, hx)
+        assert out["s_row"][r, 1] == sc and list(out["q_row"][r, 32:64]) == list(q)
+    hx = oracle.hadamard32(x[:, 7], signs)
+    sc, q = oracle.quantize_block(oracle.E4M3, hx)
+    assert out["s_colt"][7, 0] == sc and list(out["q_colt"][7]) == list(q)
+
+
+# --------------------------------------------------------------------------
+# dequantize
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("fmt", range(6))
+def test_dequantize_is_scale_times_element(oracle, fmt):
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal((4, 64)).astype(np.float32)
+    out = oracle.quantize(x, fmt, 1)
+    out["s_row"][1, 1] = 0xFF
+    out["s_row"][2, 0] = 0
+    out["s_row"][3, 0] = 254
+    y = oracle.dequantize(out["q_row"], out["s_row"], fmt, 4, 64)
+    for r in range(4):
+        codes = unpack(out["q_row"][r], fmt, 64)
+        for j in range(64):
+            sc = int(out["s_row"][r, j // 32])
+            if sc == 0xFF:
+                assert math.isnan(y[r, j])
+                continue
+            exact = Fraction(oracle.elem_value(fmt, codes[j])) * Fraction(2) ** (sc - 127)
+            want = np.float32(float(exact)) if abs(exact) < 2 ** 128 else np.float32(np.inf) * np.sign(float(exact))
+            assert y[r, j] == want or (want == 0 and y[r, j] == 0)
+
+
+# --------------------------------------------------------------------------
+# the fp64 dot product
+# --------------------------------------------------------------------------
+def _rand_q(oracle, rng, fmt, rows, k, spread):
+    x = (rng.standard_normal((rows, k)) * np.exp2(rng.integers(-spread, spread + 1, (rows, 1)))).astype(np.float32)
+    out = oracle.quantize(x, fmt, 1)
+    return out["q_row"], out["s_row"]
+
+
+@pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0), (4, 4), (2, 3), (5, 5)])
+def test_gemm_matches_exact_rationals(oracle, fa, fb):
+    rng = np.random.default_rng(16)
+    for K in (32, 64):
+        M, N = 3, 4
+        aq, as_ = _rand_q(oracle, rng, fa, M, K, 3)
+        bq, bs = _rand_q(oracle, rng, fb, N, K, 3)
+        c, t = oracle.gemm_f64(aq, as_, fa, bq, bs, fb, M, N, K)
+        for m in range(M):
+            ca = unpack(aq[m], fa, K)
+            for n in range(N):
+                cb = unpack(bq[n], fb, K)
+                s = Fraction(0)
+                sa = Fraction(0)
+                for k in range(K):
+                    a = Fraction(oracle.elem_value(fa, ca[k])) * Fraction(2) ** (int(as_[m, k // 32]) - 127)
+                    b = Fraction(oracle.elem_value(fb, cb[k])) * Fraction(2) ** (int(bs[n, k // 32]) - 127)
+                    s += a * b
+                    sa += abs(a * b)
+                assert Fraction(c[m, n]) == s
+                assert Fraction(t[m, n]) == sa
+
+
+def test_gemm_integer_special_case(oracle):
+    """Scale 127 and integer-valued E2M1 elements: an integer matmul."""
+    rng = np.random.default_rng(17)
+    M, N, K = 8, 6, 96
+    vals = np.array([0, 1, 2, 3, 4, 6, -1, -2, -3, -4, -6], np.float32)
+    a = rng.choice(vals, (M, K)).astype(np.float32)
+    b = rng.choice(vals, (N, K)).astype(np.float32)
+    a[:, ::32] = 6.0  # pins every block's scale at 127
+    b[:, ::32] = -6.0
+    qa, qb = oracle.quantize(a, 4, 1), oracle.quantize(b, 4, 1)
+    assert (qa["s_row"] == 127).all() and (qb["s_row"] == 127).all()
+    c, _ = oracle.gemm_f64(qa["q_row"], qa["s_row"], 4, qb["q_row"], qb["s_row"], 4, M, N, K)
+    np.testing.assert_array_equal(c, a.astype(np.int64) @ b.astype(np.int64).T)
+
+
+def test_gemm_identity_pattern(oracle):
+    rng = np.random.default_rng(18)
+    M, K = 5, 64
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    qa = oracle.quantize(a, 0, 1)
+    eye = np.eye(K, dtype=np.float32)
+    qb = oracle.quantize(eye, 0, 1)
+    c, _ = oracle.gemm_f64(qa["q_row"], qa["s_row"], 0, qb["q_row"], qb["s_row"], 0, M, K, K)
+    np.testing.assert_array_equal(c, oracle.dequantize(qa["q_row"], qa["s_row"], 0, M, K))
+
+
+def test_gemm_at_matches_full(oracle):
+    rng = np.random.default_rng(19)
+    M, N, K = 7, 9, 128
+    aq, as_ = _rand_q(oracle, rng, 0, M, K, 10)
+    bq, bs = _rand_q(oracle, rng, 1, N, K, 10)
+    c, t = oracle.gemm_f64(aq, as_, 0, bq, bs, 1, M, N, K)
+    ms = rng.integers(0, M, 20)
+    ns = rng.integers(0, N, 20)
+    c2, t2 = oracle.gemm_f64_at(aq, as_, 0, bq, bs, 1, M, N, K, ms, ns)
+    np.testing.assert_array_equal(c2, c[ms, ns])
+    np.testing.assert_array_equal(t2, t[ms, ns])
