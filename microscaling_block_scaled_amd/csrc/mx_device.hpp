@@ -1,0 +1,169 @@
+// mx_device.hpp -- device-side building blocks of the MX kernels for gfx950.
+//
+// Element formats (OCP MX v1.0 / OCP FP8), block conversion steps of
+// Algorithm 1 ("Microscaling Data Formats for Deep Learning", summary section 3),
+// the Philox4x32-10 generator (Salmon et al., SC'11) used for stochastic
+// rounding, and wave-level helpers (DPP).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+// ---------------------------------------------------------------------------
+// element format traits
+// ---------------------------------------------------------------------------
+enum { E4M3 = 0, E5M2 = 1, E2M3 = 2, E3M2 = 3, E2M1 = 4, INT8 = 5 };
+
+template <int F> struct Fmt;
+// bits: storage bits; mbits: mantissa bits; bias; emin: exponent of the
+// smallest normal binade; emax: exponent of the largest normal binade;
+// maxcode: code of the largest finite magnitude; nan: code written for a
+// block whose scale is NaN.
+template <> struct Fmt<E4M3> { static constexpr int bits = 8, mbits = 3, bias = 7,  emin = -6,  emax = 8,  maxcode = 0x7E, nan = 0x7F; };
+template <> struct Fmt<E5M2> { static constexpr int bits = 8, mbits = 2, bias = 15, emin = -14, emax = 15, maxcode = 0x7B, nan = 0x7F; };
+template <> struct Fmt<E2M3> { static constexpr int bits = 6, mbits = 3, bias = 1,  emin = 0,   emax = 2,  maxcode = 0x1F, nan = 0; };
+template <> struct Fmt<E3M2> { static constexpr int bits = 6, mbits = 2, bias = 3,  emin = -2,  emax = 4,  maxcode = 0x1F, nan = 0; };
+template <> struct Fmt<E2M1> { static constexpr int bits = 4, mbits = 1, bias = 1,  emin = 0,   emax = 2,  maxcode = 0x7,  nan = 0; };
+// INT8: n / 64 with n in [-127, 127]; the scale uses emax = 0.
+template <> struct Fmt<INT8> { static constexpr int bits = 8, mbits = 0, bias = 0,  emin = 0,   emax = 0,  maxcode = 127,  nan = 0; };
+
+// Smallest scale code at which every fp32-subnormal input already rounds to
+// zero in format F: V < 2^-126 gives |V / X| < 2^(1 - code), below half of the
+// smallest grid step.  Blocks at or above it need no explicit flush before a
+// hardware conversion.
+template <int F> struct DazFree {
+  static constexpr int value = (F == INT8) ? 8 : 2 - Fmt<F>::emin + Fmt<F>::mbits;
+};
+
+// ---------------------------------------------------------------------------
+// scale (Algorithm 1: shared exponent = floor(log2 amax) - emax, E8M0)
+// ---------------------------------------------------------------------------
+// `amax_bits` is the largest |V| of the block as fp32 bits (sign cleared).
+// Inf/NaN anywhere gives a bit pattern >= 0x7F800000 and the NaN scale 0xFF.
+// A zero block (and one whose max is fp32-subnormal, which the flush turns
+// into a zero block) gets exponent field 0 and so code 0.
+template <int F>
+__device__ __forceinline__ uint32_t scale_code(uint32_t amax_bits) {
+  uint32_t e = amax_bits >> 23;
+  if (e >= 255u) return 0xFFu;
+  int c = (int)e - Fmt<F>::emax;
+  return c < 0 ? 0u : (uint32_t)c;
+}
+
+// ---------------------------------------------------------------------------
+// exact integer conversion of one element, RNE or SR
+// ---------------------------------------------------------------------------
+// `vbits`: fp32 bits of a finite, already-flushed V.  `code`: the block's scale
+// code (not 0xFF).  Computes Q(V / 2^(code-127)) on the element grid with the
+// magnitude rounded to nearest even (SR == false) or rounded up iff
+// r < floor(frac * 2^32) (SR == true), saturating at the largest normal.
+template <int F, bool SR>
+__device__ __forceinline__ uint32_t cvt_exact(uint32_t vbits, uint32_t code, uint32_t r) {
+  using T = Fmt<F>;
+  const uint32_t sign = vbits >> 31;
+  const uint32_t ab = vbits & 0x7FFFFFFFu;
+  const int Ev = (int)(ab >> 23);
+  uint32_t n = 0, up = 0;
+  int e = 0;
+  if (Ev != 0) {
+    const uint32_t m = (ab & 0x7FFFFFu) | 0x800000u;  // |V| = m * 2^(Ev - 150)
+    const int ey = Ev - (int)code;                   // exponent of |V / X|
+    int sh;
+    if (F == INT8) {
+      sh = 17 - ey;  // grid step 2^-6
+    } else {
+      e = ey < T::emin ? T::emin : ey;
+      sh = 23 - T::mbits + (e - ey);
+    }
+    if (sh < 32) {
+      n = m >> sh;
+      if (SR) {
+        const uint32_t F32 = m << (32 - sh);  // discarded fraction, top 32 bits
+        up = r < F32;
+      } else {
+        const uint32_t rem = m & ((1u << sh) - 1u);
+        const uint32_t half = 1u << (sh - 1);
+        up = (rem > half) | ((rem == half) & (n & 1u));
+      }
+    } else {
+      n = 0;
+      if (SR) {
+        const uint32_t F32 = (sh - 32 < 32) ? (m >> (sh - 32)) : 0u;
+        up = r < F32;
+      } else {
+        up = 0;  // |y| < 2^24 * 2^-32 of a step: below half
+      }
+    }
+    n += up;
+  } else {
+    e = T::emin;
+  }
+  if (F == INT8) {
+    if (n > 127u) n = 127u;
+    return sign ? ((0u - n) & 0xFFu) : n;
+  }
+  // n steps of 2^(e - mbits); for e == emin this covers subnormals and the
+  // carry into the first normal binade, and a carry to 2^(mbits+1) moves to the
+  // next binade -- all by the same sum.
+  uint32_t c = n + ((uint32_t)(e + T::bias - 1) << T::mbits);
+  if (c > (uint32_t)T::maxcode) c = T::maxcode;
+  return c | (sign << (T::bits - 1));
+}
+
+// ---------------------------------------------------------------------------
+// flush of fp32-subnormal values to signed zero
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t daz32(uint32_t b) {
+  return (b & 0x7F800000u) ? b : (b & 0x80000000u);
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10
+// ---------------------------------------------------------------------------
+struct U4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ U4 philox(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                     uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int i = 0; i < 10; i++) {
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+    k0 += 0x9E3779B9u; k1 += 0xBB67AE85u;
+  }
+  return U4{c0, c1, c2, c3};
+}
+
+// The four words for source elements 4g .. 4g+3 (g = i >> 2) of one layout.
+__device__ __forceinline__ U4 sr_words(uint64_t seed, uint64_t counter_offset, uint32_t layout,
+                                       uint64_t g) {
+  const uint64_t j = counter_offset + g;
+  return philox((uint32_t)j, (uint32_t)(j >> 32), layout, 0u, (uint32_t)seed,
+                (uint32_t)(seed >> 32));
+}
+
+// ---------------------------------------------------------------------------
+// DPP lane exchange inside groups of four lanes
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t quad_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+}
+__device__ __forceinline__ uint32_t quad_xor2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+}
+__device__ __forceinline__ float quad_xor1f(float v) {
+  return __builtin_bit_cast(float, quad_xor1(__builtin_bit_cast(uint32_t, v)));
+}
+__device__ __forceinline__ float quad_xor2f(float v) {
+  return __builtin_bit_cast(float, quad_xor2(__builtin_bit_cast(uint32_t, v)));
+}
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// fp32 value of 1/sqrt(32) rounded to nearest (0x3E3504F3).
+__device__ __forceinline__ float inv_sqrt32() { return __builtin_bit_cast(float, 0x3E3504F3u); }
+
+}  // namespace mx

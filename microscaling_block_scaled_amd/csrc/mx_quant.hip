@@ -1,0 +1,550 @@
+// mx_quant.hip -- MX block quantization kernels for gfx950 (CDNA4).
+//
+// Implements Algorithm 1 of "Microscaling Data Formats for Deep Learning"
+// (summary section 3) over 32-element blocks: shared scale from the block max
+// (E8M0), per-element conversion with saturation, fp32-subnormal inputs set to
+// zero, and the block axis chosen by the output layout.  Optional steps from
+// "Format-Aware Fusion for Fast FP4 Pretraining": stochastic rounding with a
+// counter-based generator and a fixed-sign 32-point Hadamard transform per
+// block before scaling.
+//
+// Two kernels:
+//   k_quant_rows   row-wise layout.  A lane owns 8 consecutive elements (one
+//                  16-byte bf16 load); four lanes hold one block and reduce its
+//                  max with two DPP quad exchanges.  Loads and stores of a wave
+//                  are contiguous.
+//   k_quant_tiles  column-wise layout stored transposed, optionally fused with
+//                  the row-wise one (one HBM read for both).  A 128 x 256 bf16
+//                  tile (128 x 128 fp32) is read with coalesced 16-byte loads,
+//                  row blocks are emitted from registers, the flushed tile is
+//                  staged in LDS, and each lane then owns one 32-row column
+//                  block of a few columns; four consecutive lanes write 128
+//                  contiguous bytes of a transposed output row.
+#include "mx_device.hpp"
+#include "mx_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace mx {
+
+enum { SRC_F32 = 0, SRC_BF16 = 1 };
+typedef short v2s __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// conversion of 8 elements of one block to packed codes
+// ---------------------------------------------------------------------------
+// Packed result of 8 elements: FP8 / INT8 8 bytes in w[0..1]; FP6 48 bits (w[0]
+// then the low 16 bits of w[1]); FP4 32 bits in w[0].
+struct Pack8 { uint32_t w[2]; };
+
+// gfx950's scaled conversions divide by the scale and round to nearest even.
+// For E4M3, E5M2 and E2M1 they agree bit for bit with the definition on every
+// finite non-subnormal input, except that FP8 overflow gives the NaN / Inf code
+// instead of saturating; fix_sat repairs that.  Used only for scale codes at
+// which fp32-subnormal inputs round to zero anyway (DazFree), so no flush is
+// needed first.
+template <int F>
+__device__ __forceinline__ uint32_t fix_sat(uint32_t r) {
+  if (F == E4M3) {  // 0x7F / 0xFF (NaN) -> 0x7E / 0xFE
+    const uint32_t t = r & 0x7F7F7F7Fu;
+    return r - (((t + 0x01010101u) & 0x80808080u) >> 7);
+  } else {  // E5M2: 0x7C / 0xFC (Inf) -> 0x7B / 0xFB
+    const uint32_t t = (r & 0x7F7F7F7Fu) ^ 0x7C7C7C7Cu;
+    const uint32_t nz = (((t & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | t) & 0x80808080u;
+    return r - ((~nz & 0x80808080u) >> 7);
+  }
+}
+
+template <int F>
+__device__ __forceinline__ Pack8 hw_convert8(const uint32_t v[8], uint32_t code) {
+  const float S = __builtin_bit_cast(float, code << 23);  // 2^(code - 127), code >= 1
+  float f[8];
+#pragma unroll
+  for (int k = 0; k < 8; k++) f[k] = __builtin_bit_cast(float, v[k]);
+  Pack8 o;
+  if (F == E4M3 || F == E5M2) {
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      v2s t = {0, 0};
+      if (F == E4M3) {
+        t = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(t, f[4 * h], f[4 * h + 1], S, false);
+        t = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(t, f[4 * h + 2], f[4 * h + 3], S, true);
+      } else {
+        t = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(t, f[4 * h], f[4 * h + 1], S, false);
+        t = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(t, f[4 * h + 2], f[4 * h + 3], S, true);
+      }
+      o.w[h] = fix_sat<F>(__builtin_bit_cast(uint32_t, t));
+    }
+  } else {  // E2M1: saturates in hardware
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[0], f[1], S, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[2], f[3], S, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[4], f[5], S, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[6], f[7], S, 3);
+    o.w[0] = r;
+    o.w[1] = 0;
+  }
+  return o;
+}
+
+template <int F>
+__device__ __forceinline__ Pack8 pack8(const uint32_t c[8]) {
+  Pack8 o;
+  if (Fmt<F>::bits == 8) {
+    o.w[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+    o.w[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+  } else if (Fmt<F>::bits == 4) {
+    uint32_t r = 0;
+#pragma unroll
+    for (int k = 0; k < 8; k++) r |= c[k] << (4 * k);
+    o.w[0] = r;
+    o.w[1] = 0;
+  } else {  // 6 bits, element k at bit 6k
+    o.w[0] = c[0] | (c[1] << 6) | (c[2] << 12) | (c[3] << 18) | (c[4] << 24) | (c[5] << 30);
+    o.w[1] = (c[5] >> 2) | (c[6] << 4) | (c[7] << 10);
+  }
+  return o;
+}
+
+// Codes of 8 elements of a block with scale `code`.  `v` holds fp32 bits;
+// `rnd` the stochastic-rounding words (ignored for RNE).
+template <int F, bool SR>
+__device__ __forceinline__ Pack8 convert8(const uint32_t v[8], uint32_t code, const uint32_t rnd[8]) {
+  if (code == 0xFFu) {  // NaN scale: NaN elements where the format has them
+    const uint32_t n = (uint32_t)Fmt<F>::nan;
+    uint32_t c[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) c[k] = n;
+    return pack8<F>(c);
+  }
+  if (!SR && (F == E4M3 || F == E5M2 || F == E2M1) && code >= (uint32_t)DazFree<F>::value)
+    return hw_convert8<F>(v, code);
+  uint32_t c[8];
+#pragma unroll
+  for (int k = 0; k < 8; k++) c[k] = cvt_exact<F, SR>(daz32(v[k]), code, SR ? rnd[k] : 0u);
+  return pack8<F>(c);
+}
+
+// ---------------------------------------------------------------------------
+// stores
+// ---------------------------------------------------------------------------
+// 8 codes at element offset 8 * c of a packed row.
+template <int F>
+__device__ __forceinline__ void store8(uint8_t* row, int64_t c, const Pack8& o) {
+  if (Fmt<F>::bits == 8) {
+    *(uint2*)(row + 8 * c) = make_uint2(o.w[0], o.w[1]);
+  } else if (Fmt<F>::bits == 4) {
+    *(uint32_t*)(row + 4 * c) = o.w[0];
+  } else {  // 6 bytes at 6c: dword + half, or half + dword, by parity
+    uint8_t* p = row + 6 * c;
+    if ((c & 1) == 0) {
+      *(uint32_t*)p = o.w[0];
+      *(uint16_t*)(p + 4) = (uint16_t)o.w[1];
+    } else {
+      *(uint16_t*)p = (uint16_t)o.w[0];
+      *(uint32_t*)(p + 2) = (o.w[0] >> 16) | (o.w[1] << 16);
+    }
+  }
+}
+
+// 32 codes (a whole block, four Pack8) at an aligned block position.
+template <int F>
+__device__ __forceinline__ void store32(uint8_t* p, const Pack8 o[4]) {
+  if (Fmt<F>::bits == 8) {
+    *(uint4*)p = make_uint4(o[0].w[0], o[0].w[1], o[1].w[0], o[1].w[1]);
+    *(uint4*)(p + 16) = make_uint4(o[2].w[0], o[2].w[1], o[3].w[0], o[3].w[1]);
+  } else if (Fmt<F>::bits == 4) {
+    *(uint4*)p = make_uint4(o[0].w[0], o[1].w[0], o[2].w[0], o[3].w[0]);
+  } else {  // 24 bytes, 8-byte aligned
+    const uint32_t w0 = o[0].w[0];
+    const uint32_t w1 = (o[0].w[1] & 0xFFFFu) | (o[1].w[0] << 16);
+    const uint32_t w2 = (o[1].w[0] >> 16) | (o[1].w[1] << 16);
+    const uint32_t w3 = o[2].w[0];
+    const uint32_t w4 = (o[2].w[1] & 0xFFFFu) | (o[3].w[0] << 16);
+    const uint32_t w5 = (o[3].w[0] >> 16) | (o[3].w[1] << 16);
+    *(uint2*)p = make_uint2(w0, w1);
+    *(uint2*)(p + 8) = make_uint2(w2, w3);
+    *(uint2*)(p + 16) = make_uint2(w4, w5);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Hadamard-32
+// ---------------------------------------------------------------------------
+// Block spread over a quad: lane q holds elements 8q .. 8q+7.  Stages with
+// stride 1, 2, 4 are inside the lane, 8 and 16 pair lanes q^1 and q^2.  Each
+// pair (x_j, x_{j+h}) becomes (x_j + x_{j+h}, x_j - x_{j+h}).
+__device__ __forceinline__ void hadamard_quad(uint32_t v[8], int q, uint32_t signs) {
+  float f[8];
+#pragma unroll
+  for (int k = 0; k < 8; k++)
+    f[k] = __builtin_bit_cast(float, v[k] ^ (((signs >> (8 * q + k)) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      if (k & h) continue;
+      const float a = f[k], b = f[k + h];
+      f[k] = a + b;
+      f[k + h] = a - b;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    const float o = quad_xor1f(f[k]);
+    f[k] = (q & 1) ? (o - f[k]) : (f[k] + o);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    const float o = quad_xor2f(f[k]);
+    f[k] = (q & 2) ? (o - f[k]) : (f[k] + o);
+  }
+  const float c = inv_sqrt32();
+#pragma unroll
+  for (int k = 0; k < 8; k++) v[k] = __builtin_bit_cast(uint32_t, f[k] * c);
+}
+
+// Whole block in one lane.
+__device__ __forceinline__ void hadamard_local(uint32_t v[32], uint32_t signs) {
+  float f[32];
+#pragma unroll
+  for (int k = 0; k < 32; k++) f[k] = __builtin_bit_cast(float, v[k] ^ (((signs >> k) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int k = 0; k < 32; k++) {
+      if (k & h) continue;
+      const float a = f[k], b = f[k + h];
+      f[k] = a + b;
+      f[k + h] = a - b;
+    }
+  }
+  const float c = inv_sqrt32();
+#pragma unroll
+  for (int k = 0; k < 32; k++) v[k] = __builtin_bit_cast(uint32_t, f[k] * c);
+}
+
+// ---------------------------------------------------------------------------
+// shared per-chunk row-wise step
+// ---------------------------------------------------------------------------
+struct QP {
+  const uint8_t* x;
+  int64_t rows, cols, ld_bytes;
+  uint8_t* q_row;
+  int64_t qr_pitch;  // bytes per packed output row (row-wise layout)
+  uint8_t* s_row;
+  uint8_t* q_colt;
+  int64_t qc_pitch;  // bytes per packed output row (transposed layout)
+  uint8_t* s_colt;
+  uint64_t seed, off;
+  uint32_t signs;
+  int lpr_log2;        // rows kernel: lanes per row (log2)
+  int rows_per_block;  // rows kernel
+  int tiles_c;         // tile kernel: tiles along columns
+};
+
+template <int SRC>
+__device__ __forceinline__ void widen8(const uint32_t* raw, uint32_t v[8]) {
+  if (SRC == SRC_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      v[2 * i] = raw[i] << 16;
+      v[2 * i + 1] = raw[i] & 0xFFFF0000u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = raw[i];
+  }
+}
+
+// Quantize the 8 elements v (fp32 bits) at row r, chunk c (elements 8c..8c+7)
+// into the row-wise layout.  The four lanes of the block are one DPP quad, q =
+// c & 3 is this lane's place in it.  All four lanes must be active.
+template <int F, bool SR, bool HAD>
+__device__ __forceinline__ void row_chunk(const QP& p, int64_t r, int64_t c, uint32_t v[8]) {
+  const int q = (int)(c & 3);
+  if (HAD) {
+#pragma unroll
+    for (int k = 0; k < 8; k++) v[k] = daz32(v[k]);
+    hadamard_quad(v, q, p.signs);
+#pragma unroll
+    for (int k = 0; k < 8; k++) v[k] = daz32(v[k]);
+  }
+  uint32_t am = 0;
+#pragma unroll
+  for (int k = 0; k < 8; k++) am = umax(am, v[k] & 0x7FFFFFFFu);
+  am = umax(am, quad_xor1(am));
+  am = umax(am, quad_xor2(am));
+  const uint32_t code = scale_code<F>(am);
+  if (q == 0) p.s_row[r * (p.cols >> 5) + (c >> 2)] = (uint8_t)code;
+  uint32_t rnd[8];
+  if (SR) {
+    const uint64_t g = (uint64_t)(r * p.cols + 8 * c) >> 2;
+    const U4 a = sr_words(p.seed, p.off, 0u, g);
+    const U4 b = sr_words(p.seed, p.off, 0u, g + 1);
+    rnd[0] = a.x; rnd[1] = a.y; rnd[2] = a.z; rnd[3] = a.w;
+    rnd[4] = b.x; rnd[5] = b.y; rnd[6] = b.z; rnd[7] = b.w;
+  }
+  const Pack8 o = convert8<F, SR>(v, code, rnd);
+  store8<F>(p.q_row + r * p.qr_pitch, c, o);
+}
+
+// ---------------------------------------------------------------------------
+// row-wise kernel
+// ---------------------------------------------------------------------------
+template <int SRC>
+__device__ __forceinline__ void load8(const uint8_t* rowp, int64_t c, uint32_t raw[8]) {
+  if (SRC == SRC_BF16) {
+    const uint4 t = *(const uint4*)(rowp + 16 * c);
+    raw[0] = t.x; raw[1] = t.y; raw[2] = t.z; raw[3] = t.w;
+  } else {
+    const uint4 t0 = *(const uint4*)(rowp + 32 * c);
+    const uint4 t1 = *(const uint4*)(rowp + 32 * c + 16);
+    raw[0] = t0.x; raw[1] = t0.y; raw[2] = t0.z; raw[3] = t0.w;
+    raw[4] = t1.x; raw[5] = t1.y; raw[6] = t1.z; raw[7] = t1.w;
+  }
+}
+
+constexpr int ROW_UNROLL = 4;
+
+template <int SRC, int F, bool SR, bool HAD>
+__global__ __launch_bounds__(256) void k_quant_rows(QP p) {
+  const int lpr = 1 << p.lpr_log2;
+  const int tid = threadIdx.x;
+  const int lr = tid & (lpr - 1);
+  const int rpp = 256 >> p.lpr_log2;
+  const int64_t cpr = p.cols >> 3;  // 8-element chunks per row
+  const int64_t r0 = (int64_t)blockIdx.x * p.rows_per_block;
+  const int64_t r1 = r0 + p.rows_per_block < p.rows ? r0 + p.rows_per_block : p.rows;
+  for (int64_t r = r0 + (tid >> p.lpr_log2); r < r1; r += rpp) {
+    const uint8_t* rowp = p.x + r * p.ld_bytes;
+    for (int64_t c = lr; c < cpr; c += (int64_t)lpr * ROW_UNROLL) {
+      uint32_t raw[ROW_UNROLL][8];
+#pragma unroll
+      for (int u = 0; u < ROW_UNROLL; u++)
+        if (c + u * lpr < cpr) load8<SRC>(rowp, c + u * lpr, raw[u]);
+#pragma unroll
+      for (int u = 0; u < ROW_UNROLL; u++) {
+        if (c + u * lpr < cpr) {
+          uint32_t v[8];
+          widen8<SRC>(raw[u], v);
+          row_chunk<F, SR, HAD>(p, r, c + u * lpr, v);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// tile kernel: transposed column-wise layout, optionally fused with row-wise
+// ---------------------------------------------------------------------------
+template <int SRC> struct TileShape {
+  static constexpr int ESZ = SRC == SRC_BF16 ? 2 : 4;  // source bytes per element
+  static constexpr int TC = SRC == SRC_BF16 ? 256 : 128;
+  static constexpr int TR = 128;
+  static constexpr int CPRW = TC / 8;          // 8-element chunks per tile row
+  static constexpr int RPP = 256 / CPRW;       // tile rows per load pass
+  static constexpr int PASSES = TR / RPP;
+  static constexpr int RAWN = SRC == SRC_BF16 ? 4 : 8;  // dwords per chunk
+  static constexpr int CPT = SRC == SRC_BF16 ? 4 : 2;   // columns per lane, column pass
+  static constexpr int PITCH = TC * ESZ + 16;  // LDS row pitch, padded
+};
+
+template <int F, bool SR, bool HAD>
+__device__ __forceinline__ void col_block(const QP& p, uint32_t v[32], int64_t col, int64_t rs) {
+  if (HAD) {
+#pragma unroll
+    for (int k = 0; k < 32; k++) v[k] = daz32(v[k]);
+    hadamard_local(v, p.signs);
+#pragma unroll
+    for (int k = 0; k < 32; k++) v[k] = daz32(v[k]);
+  }
+  uint32_t am = 0;
+#pragma unroll
+  for (int k = 0; k < 32; k++) am = umax(am, v[k] & 0x7FFFFFFFu);
+  const uint32_t code = scale_code<F>(am);
+  p.s_colt[col * (p.rows >> 5) + (rs >> 5)] = (uint8_t)code;
+  Pack8 o[4];
+#pragma unroll
+  for (int h = 0; h < 4; h++) {
+    uint32_t rnd[8];
+    if (SR) {
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        const uint64_t i = (uint64_t)((rs + 8 * h + k) * p.cols + col);
+        const U4 w = sr_words(p.seed, p.off, 1u, i >> 2);
+        const uint32_t s = (uint32_t)(i & 3);
+        rnd[k] = s == 0 ? w.x : (s == 1 ? w.y : (s == 2 ? w.z : w.w));
+      }
+    }
+    o[h] = convert8<F, SR>(&v[8 * h], code, rnd);
+  }
+  store32<F>(p.q_colt + col * p.qc_pitch + (rs * Fmt<F>::bits) / 8, o);
+}
+
+template <int SRC, int F, bool SR, bool HAD, bool ROWS>
+__global__ __launch_bounds__(256) void k_quant_tiles(QP p) {
+  using T = TileShape<SRC>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[T::TR * T::PITCH];
+  const int tid = threadIdx.x;
+  const int64_t tr = blockIdx.x / p.tiles_c, tc = blockIdx.x % p.tiles_c;
+  const int64_t r0 = tr * T::TR, c0 = tc * T::TC;
+  const int tr_eff = (int)(p.rows - r0 < T::TR ? p.rows - r0 : T::TR);
+  const int tc_eff = (int)(p.cols - c0 < T::TC ? p.cols - c0 : T::TC);
+  const int cq = tid % T::CPRW, sub = tid / T::CPRW;
+  const bool col_ok = cq * 8 < tc_eff;
+
+  uint32_t raw[T::PASSES][T::RAWN];
+#pragma unroll
+  for (int pp = 0; pp < T::PASSES; pp++) {
+    const int row = pp * T::RPP + sub;
+    if (row < tr_eff && col_ok) {
+      const uint8_t* src = p.x + (r0 + row) * p.ld_bytes + c0 * T::ESZ;
+      if (SRC == SRC_BF16) {
+        const uint4 t = *(const uint4*)(src + 16 * cq);
+        raw[pp][0] = t.x; raw[pp][1] = t.y; raw[pp][2] = t.z; raw[pp][3] = t.w;
+      } else {
+        const uint4 t0 = *(const uint4*)(src + 32 * cq);
+        const uint4 t1 = *(const uint4*)(src + 32 * cq + 16);
+        raw[pp][0] = t0.x; raw[pp][1] = t0.y; raw[pp][2] = t0.z; raw[pp][3] = t0.w;
+        raw[pp][4] = t1.x; raw[pp][5] = t1.y; raw[pp][6] = t1.z; raw[pp][7] = t1.w;
+      }
+    }
+  }
+#pragma unroll
+  for (int pp = 0; pp < T::PASSES; pp++) {
+    const int row = pp * T::RPP + sub;
+    if (row < tr_eff && col_ok) {
+      uint32_t v[8];
+      widen8<SRC>(raw[pp], v);
+      if (ROWS) {
+        uint32_t w[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) w[k] = v[k];
+        row_chunk<F, SR, HAD>(p, r0 + row, (c0 >> 3) + cq, w);
+      }
+      uint8_t* dst = lds + row * T::PITCH + cq * 8 * T::ESZ;
+      if (SRC == SRC_BF16) {
+        uint32_t d[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+          d[i] = (daz32(v[2 * i]) >> 16) | (daz32(v[2 * i + 1]) & 0xFFFF0000u);
+        *(uint4*)dst = make_uint4(d[0], d[1], d[2], d[3]);
+      } else {
+        *(uint4*)dst = make_uint4(daz32(v[0]), daz32(v[1]), daz32(v[2]), daz32(v[3]));
+        *(uint4*)(dst + 16) = make_uint4(daz32(v[4]), daz32(v[5]), daz32(v[6]), daz32(v[7]));
+      }
+    }
+  }
+  __syncthreads();
+
+  const int qb = tid & 3, g = tid >> 2;
+  if (32 * qb < tr_eff && g * T::CPT < tc_eff) {
+#pragma unroll 1
+    for (int k = 0; k < T::CPT; k++) {
+      const int lc = g * T::CPT + k;
+      uint32_t v[32];
+#pragma unroll
+      for (int i = 0; i < 32; i++) {
+        const uint8_t* s = lds + (32 * qb + i) * T::PITCH + lc * T::ESZ;
+        v[i] = SRC == SRC_BF16 ? ((uint32_t)(*(const uint16_t*)s) << 16) : *(const uint32_t*)s;
+      }
+      col_block<F, SR, HAD>(p, v, c0 + lc, r0 + 32 * qb);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+static QP make_qp(const QuantArgs& a) {
+  QP p{};
+  p.x = (const uint8_t*)a.x;
+  p.rows = a.rows;
+  p.cols = a.cols;
+  p.ld_bytes = a.ld_bytes;
+  const int bits = elem_bits(a.fmt);
+  p.q_row = a.q_row;
+  p.qr_pitch = a.cols * bits / 8;
+  p.s_row = a.s_row;
+  p.q_colt = a.q_colt;
+  p.qc_pitch = a.rows * bits / 8;
+  p.s_colt = a.s_colt;
+  p.seed = a.seed;
+  p.off = a.counter_offset;
+  p.signs = a.signs;
+  return p;
+}
+
+template <int SRC, int F, bool SR, bool HAD>
+static hipError_t rows_launch(const QP& p0, hipStream_t st) {
+  QP p = p0;
+  const int64_t cpr = p.cols / 8;
+  int lg = 6;  // up to a wave per row
+  while (lg > 2 && ((int64_t)1 << lg) > cpr) lg--;
+  p.lpr_log2 = lg;
+  const int rpp = 256 >> lg;
+  p.rows_per_block = rpp;
+  const int64_t blocks = (p.rows + p.rows_per_block - 1) / p.rows_per_block;
+  hipLaunchKernelGGL((k_quant_rows<SRC, F, SR, HAD>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+template <int SRC, int F, bool SR, bool HAD>
+static hipError_t tiles_launch(const QP& p0, bool rows, hipStream_t st) {
+  using T = TileShape<SRC>;
+  QP p = p0;
+  const int64_t tiles_r = (p.rows + T::TR - 1) / T::TR;
+  const int64_t tiles_c = (p.cols + T::TC - 1) / T::TC;
+  p.tiles_c = (int)tiles_c;
+  const dim3 grid((unsigned)(tiles_r * tiles_c));
+  if (rows)
+    hipLaunchKernelGGL((k_quant_tiles<SRC, F, SR, HAD, true>), grid, dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((k_quant_tiles<SRC, F, SR, HAD, false>), grid, dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+// Dispatch over (source, format, rounding, Hadamard) to a templated launcher.
+template <template <int, int, bool, bool> class L, typename... A>
+static hipError_t dispatch(int src, int fmt, bool sr, bool had, A... args) {
+#define MX_DISPATCH_F(S, FM)                                                     \
+  if (!sr && !had) return L<S, FM, false, false>::run(args...);                  \
+  if (!sr && had) return L<S, FM, false, true>::run(args...);                    \
+  if (sr && !had) return L<S, FM, true, false>::run(args...);                    \
+  return L<S, FM, true, true>::run(args...);
+#define MX_DISPATCH_S(S)                    \
+  switch (fmt) {                            \
+    case E4M3: { MX_DISPATCH_F(S, E4M3) }   \
+    case E5M2: { MX_DISPATCH_F(S, E5M2) }   \
+    case E2M3: { MX_DISPATCH_F(S, E2M3) }   \
+    case E3M2: { MX_DISPATCH_F(S, E3M2) }   \
+    case E2M1: { MX_DISPATCH_F(S, E2M1) }   \
+    default: { MX_DISPATCH_F(S, INT8) }     \
+  }
+  if (src == SRC_BF16) { MX_DISPATCH_S(SRC_BF16) }
+  MX_DISPATCH_S(SRC_F32)
+#undef MX_DISPATCH_S
+#undef MX_DISPATCH_F
+}
+
+template <int SRC, int F, bool SR, bool HAD> struct RowsL {
+  static hipError_t run(const QP& p, hipStream_t st) { return rows_launch<SRC, F, SR, HAD>(p, st); }
+};
+template <int SRC, int F, bool SR, bool HAD> struct TilesL {
+  static hipError_t run(const QP& p, bool rows, hipStream_t st) {
+    return tiles_launch<SRC, F, SR, HAD>(p, rows, st);
+  }
+};
+
+hipError_t launch_quant_rows(const QuantArgs& a, hipStream_t st) {
+  const QP p = make_qp(a);
+  return dispatch<RowsL>(a.src, a.fmt, a.round == 1, a.hadamard, p, st);
+}
+
+hipError_t launch_quant_tiles(const QuantArgs& a, bool with_rows, hipStream_t st) {
+  const QP p = make_qp(a);
+  return dispatch<TilesL>(a.src, a.fmt, a.round == 1, a.hadamard, p, with_rows, st);
+}
+
+}  // namespace mx
