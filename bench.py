@@ -223,7 +223,7 @@ def main():
             "M": M, "N": N, "K": K, "block": 32,
         },
         "roofline": {
-            "kernel": "k_gemm<E2M1,E2M1>",
+            "kernel": "k_gemm_fast<E2M1,E2M1,256>",
             "bound": "mfma",
             "achieved": round(gemm_tf, 1),
             "peak": PEAK_TFLOPS["fp4"],

@@ -216,65 +216,63 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ aq,
 }
 
 // ---------------------------------------------------------------------------
-// fast path (K % 128 == 0, scale rows 4-byte aligned): operand panels and scale
-// bytes go global -> LDS directly (no register staging), through a ring of NST
-// LDS stages, so loads run NST - 1 K-steps ahead of the matrix instructions.
-// One barrier per K-step.  Panel rows are stored unpadded with their 16-byte
-// chunks XOR-swizzled so that the 16 rows a 16-lane group reads fall on
-// distinct LDS banks.
+// fast path (K % 512 == 0, scale arrays 16-byte aligned, operands < 4 GiB)
+//
+// A 512-thread workgroup computes a 256 x 256 tile of C.  Per stage of KS
+// elements of K (256 when both operands are FP4, so that every operand row of
+// a stage is one 128-byte line; else 128) the A and B panels (256 rows each)
+// go global -> LDS directly (buffer_load ... lds; rows past the matrix edge
+// fall outside the buffer and read zero) into a ring of NST stages, issued
+// NST - 1 stages ahead.  Panel rows are stored unpadded with their 16-byte
+// chunks XOR-swizzled so that the rows read at one K offset hit distinct LDS
+// banks.  The E8M0 scales travel separately, 32 bytes (1024 elements of K) per
+// row at a time, into two alternating LDS buffers: one 16-byte load per lane
+// pair and row instead of a few bytes per row and stage.
+//
+// The eight waves own 128 x 64 pieces of the tile and form two groups of four
+// (one wave of each group per SIMD) that alternate roles every phase: while
+// group 0 issues the matrix instructions of one 64-element substep, group 1
+// reads its operands of that substep from LDS, and the other way round in the
+// next phase.  So on every SIMD one wave feeds the matrix unit while the other
+// moves data.  B is passed as the instruction's first operand so that a
+// lane's results are four consecutive columns of C (16-byte stores).
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) const void* gbl_ptr_t;
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int LDS_MAX = 160 * 1024;
 
-template <int F>
-__device__ __forceinline__ int swz(int r) {
-  if (Op<F>::CH == 8) return (r >> 1) & 7;
-  if (Op<F>::CH == 4) return (r >> 2) & 3;
-  return 0;  // FP6 rows (6 chunks): unswizzled
-}
-
-template <int FA, int FB> struct FastLds {
-  static constexpr int A_OFF = 0;
-  static constexpr int B_OFF = 256 * Op<FA>::RB;
-  static constexpr int SA_OFF = B_OFF + 256 * Op<FB>::RB;
-  static constexpr int SB_OFF = SA_OFF + 1024;
-  static constexpr int STAGE = SB_OFF + 1024;
-  static constexpr int NST0 = LDS_MAX / STAGE;
+template <int FA, int FB, int KS_> struct Fast {
+  static constexpr int KS = KS_;                      // K elements per stage
+  static constexpr int SUB = KS / 64;                 // 32x32x64 substeps per stage
+  static constexpr int RBA = KS * Fmt<FA>::bits / 8;  // bytes per operand row per stage
+  static constexpr int RBB = KS * Fmt<FB>::bits / 8;
+  static constexpr int CHA = RBA / 16, CHB = RBB / 16;  // 16-byte chunks per row
+  static constexpr int A_OFF = 0, B_OFF = 256 * RBA;
+  static constexpr int STAGE = 256 * (RBA + RBB);
+  static constexpr int SC_ROW = 32;                   // scale bytes per row per chunk
+  static constexpr int SPC = SC_ROW * 32 / KS;        // stages per scale chunk
+  static constexpr int SC_BUF = 512 * SC_ROW;         // one chunk: 256 A rows, then 256 B rows
+  static constexpr int NST0 = (LDS_MAX - 2 * SC_BUF) / STAGE;
   static constexpr int NST = NST0 > 4 ? 4 : NST0;
-  static constexpr int TOTAL = NST * STAGE;
-  // direct-load instructions one wave issues per K-step
-  static constexpr int PER_STEP = Op<FA>::CH + Op<FB>::CH + 2;
+  static constexpr int SC_OFF = NST * STAGE;
+  static constexpr int TOTAL = SC_OFF + 2 * SC_BUF;
+  // 1 KB panel segments per stage (4 (CHA + CHB)), shared out over 8 waves
+  static constexpr int SEG_A = 4 * CHA;
+  static constexpr int SEGS = (CHA + CHB) / 2;
+  static_assert((CHA + CHB) % 2 == 0, "panel segments split evenly over 8 waves");
+  static_assert(NST >= 2 && SPC >= NST, "stage ring and scale buffers");
 };
 
-// One panel of one K-step: 256 rows x RB bytes, 4 waves x CH instructions of
-// 64 lanes x 16 bytes.  Lane `lane` of segment I = 4p + wave fills physical
-// chunk I * 64 + lane of the panel.  Loads go through a buffer resource whose
-// size is the operand's byte count: rows past the matrix edge fall outside it
-// and read as zero.  Per lane and p only the 32-bit byte offset of the row
-// chunk is kept; the K-step's byte offset rides in the scalar offset.
-template <int F> struct PanelSrc {
-  uint32_t voff[Op<F>::CH];
-};
-
-template <int F>
-__device__ __forceinline__ void panel_src(PanelSrc<F>& P, int64_t row0, int64_t rowbytes, int wave,
-                                          int lane) {
-  using O = Op<F>;
-#pragma unroll
-  for (int p = 0; p < O::CH; p++) {
-    const int L = (p * 4 + wave) * 64 + lane;
-    const int r = L / O::CH, pc = L % O::CH;
-    const int c = pc ^ swz<F>(r);
-    P.voff[p] = (uint32_t)((row0 + r) * rowbytes + 16 * c);
-  }
+template <int CH>
+__device__ __forceinline__ int swz(int r) {
+  if (CH == 8) return (r >> 1) & 7;  // 128-byte rows
+  if (CH == 4) return (r >> 2) & 3;  // 64-byte rows
+  return 0;                          // 96-byte FP6 rows: unswizzled
 }
-
-typedef int v4i __attribute__((ext_vector_type(4)));
 
 // Raw buffer resource over `bytes` bytes at `p` (gfx9 word 3: 32-bit data),
-// held in scalar registers.
+// in scalar registers.
 __device__ __forceinline__ v4i make_rsrc(const void* p, uint32_t bytes) {
   const uint64_t a = (uint64_t)p;
   v4i r;
@@ -286,75 +284,82 @@ __device__ __forceinline__ v4i make_rsrc(const void* p, uint32_t bytes) {
 }
 
 // Buffer load of `voff` (+ scalar `soff`) straight into LDS at `lds_dst`
-// (wave-uniform; lane i lands at lds_dst + i * size).  Written as one asm block
-// that also sets M0, so the compiler does not model it: every wait on it is
-// explicit (wait_vm_barrier) and LDS reads of the filled stage come after the
-// asm barrier.  The instruction has no register result.
+// (wave-uniform; lane i lands at lds_dst + 16 i).  One asm block that also
+// sets M0, so the compiler does not model it: every wait on it is explicit,
+// and LDS reads of the filled stage come after an asm barrier.  The
+// instruction has no register result.  A load that takes its LDS address
+// from M0 needs one wait state after the write of M0.
 __device__ __forceinline__ void dma16(v4i rs, uint32_t voff, uint32_t soff, uint32_t lds_dst) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
                :
                : "v"(voff), "s"(rs), "s"(lds_dst), "s"(soff)
                : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(v4i rs, uint32_t voff, uint32_t soff, uint32_t lds_dst) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, %3 offen lds"
-               :
-               : "v"(voff), "s"(rs), "s"(lds_dst), "s"(soff)
-               : "memory", "m0");
+// The same for the lanes of `exec` when `on` is nonzero, else for no lane.
+__device__ __forceinline__ void dma16_if(v4i rs, uint32_t voff, uint32_t soff, uint32_t lds_dst,
+                                         int on) {
+  uint64_t saved;
+  asm volatile(
+      "s_mov_b32 m0, %3\n\t"
+      "s_mov_b64 %0, exec\n\t"
+      "s_cmp_lg_u32 %5, 0\n\t"
+      "s_cselect_b64 exec, exec, 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %4 offen lds\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rs), "s"(lds_dst), "s"(soff), "s"(__builtin_amdgcn_readfirstlane(on))
+      : "memory", "m0", "scc");
+}
+
+// Workgroup barrier as one asm block with a memory clobber: the compiler can
+// neither move LDS accesses across it nor add waits of its own.  The
+// scheduling fences keep the matrix instructions (not memory operations, so
+// unaffected by the clobber) on their side of it.
+__device__ __forceinline__ void barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" : : : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+// Barrier after this wave's buffer->LDS loads are down to at most n in flight
+// and its own LDS reads are back.
+template <int n>
+__device__ __forceinline__ void wait_all_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(n) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-template <int F>
-__device__ __forceinline__ void issue_panel(uint8_t* panel, v4i rs, const PanelSrc<F>& P,
-                                            uint32_t kbyte0, int wave) {
-  using O = Op<F>;
-  const uint32_t base = lds_addr(panel);
-#pragma unroll
-  for (int p = 0; p < O::CH; p++)
-    dma16(rs, P.voff[p], kbyte0, base + (uint32_t)((p * 4 + wave) * 1024));
-}
-
-// Four scale bytes (the K-step's four blocks) of panel row wave * 64 + lane.
-__device__ __forceinline__ void issue_scales(uint8_t* sp, v4i rs, uint32_t voff, uint32_t b0,
-                                             int wave) {
-  dma4(rs, voff, b0, lds_addr(sp) + (uint32_t)(wave * 256));
-}
-
-// Operand of one 16-row tile: `lb` is this lane's row start in the panel
-// (tile 0), `toff` the tile's byte offset (a constant), c0 / c1 the swizzled
-// chunks of the lane's block.
-template <int F>
-__device__ __forceinline__ v8i read_fast(const uint8_t* lb, int toff, int c0, int c1, int kb) {
-  using O = Op<F>;
+// Operand of one 32-row tile for substep u of a stage: lane l = row l % 32 of
+// the tile, block kb = l / 32 of the substep.  FP8 lanes hold the 16-byte
+// pieces at K offsets 16 kb and 32 + 16 kb of the substep; FP6 / FP4 lanes
+// hold their block.  `lb` points at the lane's row, whose chunks are swizzled
+// with `sw`.
+template <int F, int CH>
+__device__ __forceinline__ v8i read32(const uint8_t* lb, int toff, int u, int kb, int sw) {
+  constexpr int bits = Fmt<F>::bits;
   const uint8_t* base = lb + toff;
   v8i v = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (O::bits == 8) {
-    const uint4 a = *(const uint4*)(base + 16 * c0);
-    const uint4 b = *(const uint4*)(base + 16 * c1);
+  if (bits == 8) {
+    const uint4 a = *(const uint4*)(base + 16 * ((4 * u + kb) ^ sw));
+    const uint4 b = *(const uint4*)(base + 16 * ((4 * u + 2 + kb) ^ sw));
     v[0] = (int)a.x; v[1] = (int)a.y; v[2] = (int)a.z; v[3] = (int)a.w;
     v[4] = (int)b.x; v[5] = (int)b.y; v[6] = (int)b.z; v[7] = (int)b.w;
-  } else if (O::bits == 4) {
-    const uint4 a = *(const uint4*)(base + 16 * c0);
+  } else if (bits == 4) {
+    const uint4 a = *(const uint4*)(base + 16 * ((2 * u + kb) ^ sw));
     v[0] = (int)a.x; v[1] = (int)a.y; v[2] = (int)a.z; v[3] = (int)a.w;
   } else {
-    const uint2 a = *(const uint2*)(base + 24 * kb);
-    const uint2 b = *(const uint2*)(base + 24 * kb + 8);
-    const uint2 c = *(const uint2*)(base + 24 * kb + 16);
+    const uint8_t* q = base + 24 * (2 * u + kb);
+    const uint2 a = *(const uint2*)q;
+    const uint2 b = *(const uint2*)(q + 8);
+    const uint2 c = *(const uint2*)(q + 16);
     v[0] = (int)a.x; v[1] = (int)a.y; v[2] = (int)b.x; v[3] = (int)b.y;
     v[4] = (int)c.x; v[5] = (int)c.y;
   }
   return v;
-}
-
-// Wait until at most n of this wave's buffer->LDS loads are outstanding, then
-// the workgroup barrier.  One asm block with a memory clobber: the compiler
-// can neither move LDS reads above it nor add waits of its own.
-template <int n>
-__device__ __forceinline__ void wait_vm_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(n) : "memory");
 }
 
 // Workgroup -> C tile.  Workgroups are dispatched to the 8 XCDs round-robin;
@@ -375,164 +380,242 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
   tn = w / gm;
 }
 
-typedef float v16f __attribute__((ext_vector_type(16)));
+// Operands of one substep for one wave: 4 A tiles and 2 B tiles of 32 rows.
+struct Ops {
+  v8i a[4], b[2];
+  int sa[4], sb[2];
+};
 
-// Operand of one 32-row tile for the 32x32x64 instruction, half-step u of the
-// K-step (K-step elements [64u, 64u + 64)).  Lane l: row l % 32, block
-// kb = l / 32 of the half-step.  FP8 lanes hold the 16-byte pieces at K offsets
-// 16 kb and 32 + 16 kb of the half-step; FP6 / FP4 lanes hold their block.
-template <int F>
-__device__ __forceinline__ v8i read32(const uint8_t* lb, int toff, int u, int kb, int sw) {
-  using O = Op<F>;
-  const uint8_t* base = lb + toff;
-  v8i v = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (O::bits == 8) {
-    const uint4 a = *(const uint4*)(base + 16 * ((4 * u + kb) ^ sw));
-    const uint4 b = *(const uint4*)(base + 16 * ((4 * u + 2 + kb) ^ sw));
-    v[0] = (int)a.x; v[1] = (int)a.y; v[2] = (int)a.z; v[3] = (int)a.w;
-    v[4] = (int)b.x; v[5] = (int)b.y; v[6] = (int)b.z; v[7] = (int)b.w;
-  } else if (O::bits == 4) {
-    const uint4 a = *(const uint4*)(base + 16 * ((2 * u + kb) ^ sw));
-    v[0] = (int)a.x; v[1] = (int)a.y; v[2] = (int)a.z; v[3] = (int)a.w;
-  } else {
-    const uint8_t* q = base + 24 * (2 * u + kb);
-    const uint2 a = *(const uint2*)q;
-    const uint2 b = *(const uint2*)(q + 8);
-    const uint2 c = *(const uint2*)(q + 16);
-    v[0] = (int)a.x; v[1] = (int)a.y; v[2] = (int)b.x; v[3] = (int)b.y;
-    v[4] = (int)c.x; v[5] = (int)c.y;
+// Where a wave's operands sit in LDS: its rows' offsets and swizzles.
+struct Lanes {
+  int arow, brow;  // first A / B row of the wave's tiles for this lane
+  int kb, swa, swb;
+};
+
+// Operands of substep u of stage s.
+template <class C, int FA, int FB>
+__device__ __forceinline__ void read_ops(Ops& o, const uint8_t* lds, int s, int u, const Lanes& w) {
+  const uint8_t* st = lds + (s % C::NST) * C::STAGE;
+  const uint8_t* la = st + C::A_OFF + w.arow * C::RBA;
+  const uint8_t* lb = st + C::B_OFF + w.brow * C::RBB;
+  const uint8_t* sc = lds + C::SC_OFF + ((s / C::SPC) & 1) * C::SC_BUF +
+                      (s % C::SPC) * (C::KS / 32) + 2 * u + w.kb;
+  const uint8_t* sa = sc + w.arow * C::SC_ROW;
+  const uint8_t* sb = sc + (256 + w.brow) * C::SC_ROW;
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    o.b[j] = read32<FB, C::CHB>(lb, j * 32 * C::RBB, u, w.kb, w.swb);
+    o.sb[j] = sb[j * 32 * C::SC_ROW];
   }
-  return v;
-}
-
-// One K-step on LDS stage `st`: two half-steps of 4 x 4 instructions
-// (32x32x64) per wave, the A operand of tile i + 1 read from LDS while the
-// instructions of tile i issue.
-template <int FA, int FB>
-__device__ __forceinline__ void mma_step(const uint8_t* st, v16f (&acc)[4][4], int arow_off,
-                                         int brow_off, int kb, int swa, int swb) {
-  using L = FastLds<FA, FB>;
-  const uint8_t* la = st + L::A_OFF + arow_off * Op<FA>::RB;
-  const uint8_t* lb = st + L::B_OFF + brow_off * Op<FB>::RB;
-  const uint8_t* sa = st + L::SA_OFF + arow_off * 4 + kb;
-  const uint8_t* sb = st + L::SB_OFF + brow_off * 4 + kb;
 #pragma unroll
-  for (int u = 0; u < 2; u++) {
-    v8i bop[4];
-    int bsc[4];
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      bop[j] = read32<FB>(lb, j * 32 * Op<FB>::RB, u, kb, swb);
-      bsc[j] = sb[j * 128 + 2 * u];
-    }
-    v8i aop = read32<FA>(la, 0, u, kb, swa);
-    int asc = sa[2 * u];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      v8i anx = aop;
-      int asx = asc;
-      if (i < 3) {
-        anx = read32<FA>(la, (i + 1) * 32 * Op<FA>::RB, u, kb, swa);
-        asx = sa[(i + 1) * 128 + 2 * u];
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < 4; j++)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop[j], acc[i][j], FA, FB,
-                                                                    0, asc, 0, bsc[j]);
-      __builtin_amdgcn_sched_barrier(0);
-      aop = anx;
-      asc = asx;
-    }
+  for (int i = 0; i < 4; i++) {
+    o.a[i] = read32<FA, C::CHA>(la, i * 32 * C::RBA, u, w.kb, w.swa);
+    o.sa[i] = sa[i * 32 * C::SC_ROW];
   }
 }
 
 template <int FA, int FB>
-__global__ __launch_bounds__(256) void k_gemm_fast(const uint8_t* __restrict__ aq,
+__device__ __forceinline__ void mma_ops(v16f (&acc)[4][2], const Ops& o) {
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.b[j], o.a[i], acc[i][j], FB, FA,
+                                                                  0, o.sb[j], 0, o.sa[i]);
+}
+
+template <int FA, int FB, int KS>
+__global__ __launch_bounds__(512) void k_gemm_fast(const uint8_t* __restrict__ aq,
                                                    const uint8_t* __restrict__ as,
                                                    const uint8_t* __restrict__ bq,
                                                    const uint8_t* __restrict__ bs, int64_t M,
                                                    int64_t N, int64_t K, float* __restrict__ c,
-                                                   int64_t ldc, int tiles_m, int tiles_n) {
-  using L = FastLds<FA, FB>;
-  constexpr int NST = L::NST;
-  // the LDS ring: NST stages of STAGE bytes
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[L::TOTAL];
+                                                   int64_t ldc, int tiles_m, int tiles_n,
+                                                   int vec_store) {
+  using C = Fast<FA, FB, KS>;
+  constexpr int NST = C::NST, SUB = C::SUB, SPC = C::SPC;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::TOTAL];
   const int tid = threadIdx.x, lane = tid & 63;
-  // wave index as a wave-uniform (scalar) value: LDS destinations become scalar
+  // wave index as a wave-uniform (scalar) value: LDS destinations stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const bool g1 = wave >= 4;                // role group
+  const int wm = wave & 1, wn = wave >> 1;  // 2 x 4 pieces of 128 x 64
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int64_t arow = K * Op<FA>::bits / 8, brow = K * Op<FB>::bits / 8;
+  const int64_t arow = K * Fmt<FA>::bits / 8, brow = K * Fmt<FB>::bits / 8;
   const int64_t nblk = K / 32;
   const int nk = (int)(K / KS);
 
-  PanelSrc<FA> pa;
-  PanelSrc<FB> pb;
-  panel_src<FA>(pa, m0, arow, wave, lane);
-  panel_src<FB>(pb, n0, brow, wave, lane);
+  // this wave's panel segments I = wave + 8 k (A segments first, then B);
+  // lane chunk I * 64 + lane of the panel
   const v4i ra = make_rsrc(aq, (uint32_t)(M * arow));
   const v4i rb = make_rsrc(bq, (uint32_t)(N * brow));
+  uint32_t voff[C::SEGS];
+  uint32_t lofs[C::SEGS];
+  bool isb[C::SEGS];
+#pragma unroll
+  for (int k = 0; k < C::SEGS; k++) {
+    const int I = wave + 8 * k;
+    isb[k] = I >= C::SEG_A;
+    const int Ip = isb[k] ? I - C::SEG_A : I;
+    const int ch = isb[k] ? C::CHB : C::CHA;
+    const int Lc = Ip * 64 + lane;
+    const int r = Lc / ch, pc = Lc % ch;
+    const int cc = pc ^ (isb[k] ? swz<C::CHB>(r) : swz<C::CHA>(r));
+    voff[k] = isb[k] ? (uint32_t)((n0 + r) * brow + 16 * cc) : (uint32_t)((m0 + r) * arow + 16 * cc);
+    lofs[k] = (uint32_t)((isb[k] ? C::B_OFF : C::A_OFF) + Ip * 1024);
+  }
+  // scale chunks: wave w loads A scale rows 32 w .. 32 w + 31 and the same B
+  // rows, lane pair (2 r, 2 r + 1) the two 16-byte halves of row r's 32 bytes
   const v4i rsa = make_rsrc(as, (uint32_t)(M * nblk));
   const v4i rsb = make_rsrc(bs, (uint32_t)(N * nblk));
-  const uint32_t vsa = (uint32_t)((m0 + wave * 64 + lane) * nblk);
-  const uint32_t vsb = (uint32_t)((n0 + wave * 64 + lane) * nblk);
-  auto issue_step = [&](uint8_t* st, int s) {
-    issue_panel<FA>(st + L::A_OFF, ra, pa, (uint32_t)s * (KS * Op<FA>::bits / 8), wave);
-    issue_panel<FB>(st + L::B_OFF, rb, pb, (uint32_t)s * (KS * Op<FB>::bits / 8), wave);
-    issue_scales(st + L::SA_OFF, rsa, vsa, (uint32_t)s * 4, wave);
-    issue_scales(st + L::SB_OFF, rsb, vsb, (uint32_t)s * 4, wave);
+  const uint32_t vsa = (uint32_t)((m0 + wave * 32 + (lane >> 1)) * nblk + 16 * (lane & 1));
+  const uint32_t vsb = (uint32_t)((n0 + wave * 32 + (lane >> 1)) * nblk + 16 * (lane & 1));
+  const uint32_t lds0 = lds_addr(lds);
+  // Stage s into ring slot s % NST, preceded (first stage of a chunk) by the
+  // scale chunk s / SPC into scale buffer (s / SPC) % 2.  The scale loads are
+  // issued every stage under a mask that is empty except at chunk starts, so
+  // the loop body has no branch.  A stage past the end (s >= nk) goes through
+  // an empty buffer resource: every lane reads out of range, which fetches
+  // nothing, and the slot it fills is not read again.
+  const v4i rnone = {0, 0, 0, 0x00020000};
+  auto issue = [&](int s) {
+    const bool live = s < nk;
+    const bool chunk = live && (s % SPC) == 0;
+    const uint32_t sdst = lds0 + C::SC_OFF + ((s / SPC) & 1) * C::SC_BUF + wave * 1024;
+    const uint32_t soff = chunk ? (uint32_t)(s / SPC) * C::SC_ROW : 0u;
+    dma16_if(rsa, vsa, soff, sdst, chunk);
+    dma16_if(rsb, vsb, soff, sdst + 256 * C::SC_ROW, chunk);
+    const uint32_t st = lds0 + (uint32_t)((s % NST) * C::STAGE);
+#pragma unroll
+    for (int k = 0; k < C::SEGS; k++) {
+      const uint32_t kb0 = live ? (uint32_t)s * (isb[k] ? C::RBB : C::RBA) : 0u;
+      dma16(live ? (isb[k] ? rb : ra) : rnone, voff[k], kb0, st + lofs[k]);
+    }
   };
-  auto stage = [&](int j) -> uint8_t* { return ring + j * L::STAGE; };
 
-  // per-lane swizzle of the operand rows (rows of different tiles differ by
-  // multiples of 32, which leave the swizzle unchanged)
-  const int lr32 = lane & 31, kb32 = lane >> 5;
-  const int swa = swz<FA>(lr32), swb = swz<FB>(lr32);
-  const int arow_off = wm * 128 + lr32, brow_off = wn * 128 + lr32;
+  Lanes w;
+  {
+    const int lr = lane & 31;
+    w.kb = lane >> 5;
+    w.arow = wm * 128 + lr;
+    w.brow = wn * 64 + lr;
+    w.swa = swz<C::CHA>(lr);
+    w.swb = swz<C::CHB>(lr);
+  }
 
-  v16f acc[4][4];
+  v16f acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++)
+    for (int j = 0; j < 2; j++)
 #pragma unroll
       for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
+  Ops ops;
+
+  // prologue: stages 0 .. NST-1 in flight, wait for stage 0 (a wait counts
+  // panel loads only: masked-off scale loads may or may not count, and where
+  // they do the wait is merely longer)
 #pragma unroll
-  for (int i = 0; i < NST - 1; i++)
-    if (i < nk) issue_step(stage(i), i);
-
-  int cur = 0;  // stage of step s
-  for (int s = 0; s < nk; s++) {
-    // this wave's loads for step s have landed once at most the loads of the
-    // `ahead` later steps already issued are outstanding
-    const int ahead = (s + NST - 2 < nk - 1 ? s + NST - 2 : nk - 1) - s;
-    if (NST >= 4 && ahead >= 2) wait_vm_barrier<2 * L::PER_STEP>();
-    else if (NST >= 3 && ahead >= 1) wait_vm_barrier<L::PER_STEP>();
-    else wait_vm_barrier<0>();
-    const int nxt = cur == 0 ? NST - 1 : cur - 1;  // stage of step s + NST - 1
-    if (s + NST - 1 < nk) issue_step(stage(nxt), s + NST - 1);
-    mma_step<FA, FB>(stage(cur), acc, arow_off, brow_off, kb32, swa, swb);
-    cur = cur + 1 == NST ? 0 : cur + 1;
+  for (int i = 0; i < NST; i++) issue(i);
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"((NST - 1) * C::SEGS) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  // 2 SUB phases per stage s, separated by barriers; the two groups run the
+  // same barrier sequence in separate loops.  In phase 2j group 0 computes
+  // substep (s, j) while group 1 reads it; in phase 2j + 1 group 1 computes
+  // (s, j) while group 0 reads (s, j + 1), and the last phase, which starts
+  // with the wait for stage s + 1 (this wave's loads of it landed, its own
+  // LDS reads back, then the barrier: every wave is done with slot s % NST),
+  // refills that slot with stage s + NST while group 0 reads (s + 1, 0).
+  // Every phase is unconditional, so each loop body is one basic block and
+  // the scheduling fences at the barriers keep each phase's instructions in
+  // place.  Group 0's loop runs from that last phase of stage s to the end of
+  // stage s + 1, so that no operand register lives across iterations.
+  constexpr int AHEAD = (NST - 2) * C::SEGS;  // panel loads still in flight at a wait
+  if (!g1) {
+    read_ops<C, FA, FB>(ops, lds, 0, 0, w);
+#pragma unroll
+    for (int u = 0; u < SUB; u++) {
+      barrier();
+      mma_ops<FA, FB>(acc, ops);
+      if (u + 1 < SUB) {
+        barrier();
+        read_ops<C, FA, FB>(ops, lds, 0, u + 1, w);
+      }
+    }
+    for (int s = 0; s + 1 < nk; s++) {
+      wait_all_barrier<AHEAD>();
+      read_ops<C, FA, FB>(ops, lds, s + 1, 0, w);
+      issue(s + NST);
+#pragma unroll
+      for (int u = 0; u < SUB; u++) {
+        barrier();
+        mma_ops<FA, FB>(acc, ops);
+        if (u + 1 < SUB) {
+          barrier();
+          read_ops<C, FA, FB>(ops, lds, s + 1, u + 1, w);
+        }
+      }
+    }
+    wait_all_barrier<AHEAD>();  // pairs with group 1's last wait
+  } else {
+    for (int s = 0; s < nk; s++) {
+#pragma unroll
+      for (int u = 0; u < SUB; u++) {
+        barrier();
+        read_ops<C, FA, FB>(ops, lds, s, u, w);
+        if (u + 1 < SUB) {
+          barrier();
+          mma_ops<FA, FB>(acc, ops);
+        }
+      }
+      wait_all_barrier<AHEAD>();
+      issue(s + NST);
+      mma_ops<FA, FB>(acc, ops);
+    }
   }
+  // the out-of-range loads of the last stages must be done before the
+  // workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
 
-  // 32x32 result layout: lane l holds rows 8 (v / 4) + 4 (l / 32) + v % 4,
-  // v = 0..15, of column l % 32
+  // acc[i][j] is the 32 x 32 tile C^T[n][m]: lane l holds, for v = 4q + e,
+  // C[m0 + wm*128 + 32 i + l % 32][n0 + wn*64 + 32 j + 8 q + 4 (l / 32) + e]
+  const int lr = lane & 31;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
+    const int64_t row = m0 + wm * 128 + i * 32 + lr;
+    if (row >= M) continue;
+    float* crow = c + row * ldc;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int64_t col = n0 + wn * 128 + j * 32 + lr32;
+    for (int j = 0; j < 2; j++) {
 #pragma unroll
-      for (int v = 0; v < 16; v++) {
-        const int64_t row = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * kb32 + (v & 3);
-        if (row < M && col < N) c[row * ldc + col] = acc[i][j][v];
+      for (int q = 0; q < 4; q++) {
+        const int64_t col = n0 + wn * 64 + j * 32 + 8 * q + 4 * w.kb;
+        const v16f& tt = acc[i][j];
+        if (vec_store && col + 3 < N) {
+          *(float4*)(crow + col) = make_float4(tt[4 * q], tt[4 * q + 1], tt[4 * q + 2], tt[4 * q + 3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            if (col + e < N) crow[col + e] = tt[4 * q + e];
+        }
       }
     }
   }
+}
+
+template <int FA, int FB, int KS>
+static hipError_t launch_fast(const void* aq, const uint8_t* as, const void* bq, const uint8_t* bs,
+                              int64_t M, int64_t N, int64_t K, float* c, int64_t ldc,
+                              int64_t tiles_m, int64_t tiles_n, hipStream_t st) {
+  const int vec = ((uintptr_t)c % 16) == 0 && ldc % 4 == 0;
+  hipLaunchKernelGGL((k_gemm_fast<FA, FB, KS>), dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0,
+                     st, (const uint8_t*)aq, as, (const uint8_t*)bq, bs, M, N, K, c, ldc,
+                     (int)tiles_m, (int)tiles_n, vec);
+  return hipGetLastError();
 }
 
 template <int FA, int FB>
@@ -540,16 +623,22 @@ static hipError_t gemm_launch(const void* aq, const uint8_t* as, const void* bq,
                               int64_t M, int64_t N, int64_t K, float* c, int64_t ldc,
                               hipStream_t st) {
   const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  // the fast path addresses operands with 32-bit buffer offsets (rows rounded
-  // up to whole tiles must stay below 2^32 bytes)
-  const int64_t abytes = tiles_m * BM * (K * Op<FA>::bits / 8) + K;
-  const int64_t bbytes = tiles_n * BN * (K * Op<FB>::bits / 8) + K;
-  const bool fast = K > 0 && K % KS == 0 && ((uintptr_t)as % 4) == 0 && ((uintptr_t)bs % 4) == 0 &&
-                    abytes < ((int64_t)1 << 32) && bbytes < ((int64_t)1 << 32);
+  // The fast path addresses operands and scales with 32-bit buffer offsets
+  // (rows rounded up to whole tiles, plus the reach of the last chunk, stay
+  // below 2^32 bytes) and loads scale rows 16 bytes at a time.
+  const int64_t lim = (int64_t)1 << 32;
+  const int64_t nblk = K / 32;
+  const bool fast = K > 0 && K % 512 == 0 && ((uintptr_t)as % 16) == 0 &&
+                    ((uintptr_t)bs % 16) == 0 &&
+                    tiles_m * BM * (K * Fmt<FA>::bits / 8) + K < lim &&
+                    tiles_n * BN * (K * Fmt<FB>::bits / 8) + K < lim &&
+                    tiles_m * BM * nblk + 64 < lim && tiles_n * BN * nblk + 64 < lim &&
+                    tiles_m * tiles_n < ((int64_t)1 << 31);
   if (fast) {
-    hipLaunchKernelGGL((k_gemm_fast<FA, FB>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, (const uint8_t*)aq, as, (const uint8_t*)bq, bs, M, N, K, c,
-                       ldc, (int)tiles_m, (int)tiles_n);
-    return hipGetLastError();
+    if constexpr (Fmt<FA>::bits == 4 && Fmt<FB>::bits == 4)
+      return launch_fast<FA, FB, 256>(aq, as, bq, bs, M, N, K, c, ldc, tiles_m, tiles_n, st);
+    else
+      return launch_fast<FA, FB, 128>(aq, as, bq, bs, M, N, K, c, ldc, tiles_m, tiles_n, st);
   }
   using L = GemmLds<FA, FB>;
   static bool attr_done = false;  // benign race: the call is idempotent

@@ -36,26 +36,37 @@ def gemm_tolerance(t):
     return 1e-5 * t + 2.0 ** -126
 
 
-def fp8_group_bound(a, b):
-    """Worst-case error of the FP8 block-scaled matrix instruction beyond fp32
-    rounding, for C = a @ b.T (a [M,K], b [N,K] dequantized, fp64).
+def mfma_group_bound(a, b, pairs=None):
+    """Error the block-scaled matrix instruction may add beyond fp32 rounding,
+    for C = a @ b.T (a [M,K], b [N,K] dequantized, fp64), per element of C (or
+    per (m, n) in `pairs`).
 
-    Measured on gfx950 (see the design notes): with an FP8 operand the
-    instruction adds each aligned group of 8 consecutive K products after
-    truncating every product toward zero to a multiple of 2^(E - 13), E the
-    exponent of the group's largest product; groups then add exactly.  So a
-    group of n nonzero products is off by less than (n - 1) * 2^(E - 13)."""
-    M, K = a.shape
-    out = np.zeros((M, b.shape[0]))
-    for m in range(M):
-        p = np.abs(a[m][None, :] * b)                      # [N, K]
-        g = p.reshape(b.shape[0], K // 8, 8)
-        mx = g.max(axis=2)
-        nz = (g > 0).sum(axis=2)
+    Measured on gfx950 (see the design notes): the instruction adds each
+    aligned group of 8 consecutive K products after truncating every product
+    toward zero to a multiple of q = 2^(E - 13), E the exponent of the group's
+    largest product; groups then add exactly.  Where a product is not a
+    multiple of q it may lose up to q; products that are multiples of q (for
+    E2M1 and E2M3 operands, all of them) lose nothing, so those pairs keep
+    the plain tolerance."""
+    if pairs is None:
+        ms, ns = np.repeat(np.arange(a.shape[0]), b.shape[0]), np.tile(np.arange(b.shape[0]), a.shape[0])
+        shape = (a.shape[0], b.shape[0])
+    else:
+        ms, ns = pairs
+        shape = (len(ms),)
+    K = a.shape[1]
+    out = np.zeros(len(ms))
+    step = 256
+    for i in range(0, len(ms), step):
+        p = np.abs(a[ms[i:i + step]] * b[ns[i:i + step]])        # [S, K], exact in fp64
+        g = p.reshape(p.shape[0], K // 8, 8)
+        mx = g.max(axis=2, keepdims=True)
         with np.errstate(divide="ignore"):
             e = np.where(mx > 0, np.floor(np.log2(np.where(mx > 0, mx, 1.0))), 0.0)
-        out[m] = (np.maximum(nz - 1, 0) * np.exp2(e - 13)).sum(axis=1)
-    return out
+        q = np.exp2(e - 13)
+        lost = (g / q) != np.floor(g / q)
+        out[i:i + step] = (lost * q).sum(axis=(1, 2))
+    return out.reshape(shape)
 
 
 def assert_gemm_close(c_gpu, c_ref, t_ref, what="", extra=None):

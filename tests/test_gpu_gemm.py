@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import assert_gemm_close, assert_same_bits, dev, fp8_group_bound, host, say
+from gpu_util import assert_gemm_close, assert_same_bits, dev, host, mfma_group_bound, say
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +50,9 @@ def test_small_config_end_to_end(mx, oracle):
     c = host(mx.gemm(ga["q_row"], ga["s_row"], 0, gb["q_colt"], gb["s_colt"], 0, 128, 128, 256))
     cref, t = oracle.gemm_f64(oa["q_row"], oa["s_row"], 0, ob["q_colt"], ob["s_colt"], 0,
                               128, 128, 256)
-    assert_gemm_close(c, cref, t, "mxfp8_small")
+    extra = mfma_group_bound(oracle.dequantize(oa["q_row"], oa["s_row"], 0, 128, 256).astype(np.float64),
+                             oracle.dequantize(ob["q_colt"], ob["s_colt"], 0, 128, 256).astype(np.float64))
+    assert_gemm_close(c, cref, t, "mxfp8_small", extra)
 
 
 PAIRS = [(a, b) for a in range(5) for b in range(5)]
@@ -59,22 +61,23 @@ PAIRS = [(a, b) for a in range(5) for b in range(5)]
 @pytest.mark.parametrize("fa,fb", PAIRS)
 def test_all_format_pairs_ragged(mx, oracle, fa, fb):
     """Every operand-format pair on ragged shapes: M, N not multiples of the
-    256 tile, K a multiple of 32 but not of the 128-element step.  With an FP8
-    operand and short K the instruction's own truncation (fp8_group_bound) is
-    added to the 1e-5 * sum|a*b| tolerance; FP6 / FP4 pairs get none."""
+    256 tile; K a multiple of 512 (the staged kernel, with a scale chunk cut
+    short at the end of K) and K a multiple of 32 but not of 512 (the general
+    kernel).  With an FP8 operand the instruction's own truncation
+    (mfma_group_bound) is added to the 1e-5 * sum|a*b| tolerance; it is zero
+    wherever the instruction cannot truncate."""
     rng = np.random.default_rng(10 * fa + fb)
     from microscaling_block_scaled_amd.synth import bf16_bits
-    for (M, N, K) in [(288, 320, 640), (100, 36, 608), (16, 16, 32)]:
+    for (M, N, K) in [(288, 320, 1536), (100, 36, 512), (288, 320, 640), (100, 36, 608),
+                      (16, 16, 32)]:
         a = bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
         w = bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
         (ga, oa), (gw, ow) = quant_pair(mx, oracle, a, w, fa, fb)
         say("gemm", M, N, K, FMT_NAMES[fa], FMT_NAMES[fb])
         c = host(mx.gemm(ga["q_row"], ga["s_row"], fa, gw["q_row"], gw["s_row"], fb, M, N, K))
         cref, t = oracle.gemm_f64(oa["q_row"], oa["s_row"], fa, ow["q_row"], ow["s_row"], fb, M, N, K)
-        extra = None
-        if fa < 2 or fb < 2:
-            extra = fp8_group_bound(oracle.dequantize(oa["q_row"], oa["s_row"], fa, M, K).astype(np.float64),
-                                    oracle.dequantize(ow["q_row"], ow["s_row"], fb, N, K).astype(np.float64))
+        extra = mfma_group_bound(oracle.dequantize(oa["q_row"], oa["s_row"], fa, M, K).astype(np.float64),
+                                 oracle.dequantize(ow["q_row"], ow["s_row"], fb, N, K).astype(np.float64))
         assert_gemm_close(c, cref, t, f"{FMT_NAMES[fa]}x{FMT_NAMES[fb]} {M}x{N}x{K}", extra)
 
 
@@ -90,8 +93,8 @@ def test_ldc_and_degenerate(mx, oracle):
     mx.gemm(ga["q_row"], ga["s_row"], 0, gw["q_row"], gw["s_row"], 0, M, N, K, c=c[:, :N])
     cc = host(c)
     cref, t = oracle.gemm_f64(oa["q_row"], oa["s_row"], 0, ow["q_row"], ow["s_row"], 0, M, N, K)
-    extra = fp8_group_bound(oracle.dequantize(oa["q_row"], oa["s_row"], 0, M, K).astype(np.float64),
-                            oracle.dequantize(ow["q_row"], ow["s_row"], 0, N, K).astype(np.float64))
+    extra = mfma_group_bound(oracle.dequantize(oa["q_row"], oa["s_row"], 0, M, K).astype(np.float64),
+                             oracle.dequantize(ow["q_row"], ow["s_row"], 0, N, K).astype(np.float64))
     assert_gemm_close(cc[:, :N], cref, t, "ldc", extra)
     assert (cc[:, N:] == 7.0).all()  # nothing written past N
     # K = 0: the empty sum
@@ -132,5 +135,13 @@ def test_full_size_gemm_sampled(mx, oracle, cfg):
     cs = host(c[torch.from_numpy(ms).cuda(), torch.from_numpy(ns).cuda()])
     cref, t = oracle.gemm_f64_at(oa["q_row"], oa["s_row"], fa, ow["q_row"], ow["s_row"], fw,
                                  M, N, K, ms, ns)
-    worst = assert_gemm_close(cs, cref, t, cfg)
+    # instruction truncation bound on the sampled elements (operand rows
+    # dequantized by the oracle)
+    S = len(ms)
+    ad = oracle.dequantize(np.ascontiguousarray(oa["q_row"][ms]), np.ascontiguousarray(oa["s_row"][ms]),
+                           fa, S, K).astype(np.float64)
+    wd = oracle.dequantize(np.ascontiguousarray(ow["q_row"][ns]), np.ascontiguousarray(ow["s_row"][ns]),
+                           fw, S, K).astype(np.float64)
+    extra = mfma_group_bound(ad, wd, pairs=(np.arange(S), np.arange(S)))
+    worst = assert_gemm_close(cs, cref, t, cfg, extra)
     print(f"{cfg}: worst |err| / sum|ab| = {worst:.3g}")
