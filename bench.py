@@ -15,7 +15,6 @@ Prints ONE JSON line.  Only N=1 is supported: the path runs on one GPU.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -28,15 +27,6 @@ METRIC = "MX quantize GB/s + MX-GEMM TFLOPS (MXFP8/MXFP4), % of HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0
 PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0, "fp6": 10100.0}
 M, N, K = 8192, 4096, 14336
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "microscaling_block_scaled_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
-    return h.hexdigest()[:16]
 
 
 def dev_bf16(a):
@@ -146,12 +136,12 @@ def bench_gemm(mx, name, a_host, w_host, fa, fw, peak, rounds=20):
 
 def cpu_baseline():
     """The CPU oracle, timed on a bounded sample of the same step and scaled to
-    the full step: quantize 512 rows of A (H32 + SR), 256 rows of W (H32 + RNE),
-    and the 512 x 256 dot products of their MX values (fp64)."""
+    the full step: quantize 1024 rows of A (H32 + SR), 384 rows of W (H32 + RNE),
+    and the 1024 x 384 dot products of their MX values (fp64)."""
     import numpy as np
     import oracle
     from microscaling_block_scaled_amd.synth import make
-    ra, rw = 512, 256
+    ra, rw = 1024, 384
     d = make("mxfp4_mlp", {"A": (ra, K), "W": (rw, K)})
     t0 = time.perf_counter()
     qa = oracle.quantize(d["A"], oracle.E2M1, 1, oracle.SR, oracle.FLAG_HADAMARD32, 42)
@@ -168,14 +158,20 @@ def cpu_baseline():
                       f"({t3 - t0:.1f} s), scaled to the full step ({full:.0f} s)"}
 
 
+GEMM_KERNEL = "void mx::k_gemm_fast<4, 4, 256>"
+
+
 def load_traffic(src_hash):
+    """Counter-measured bytes per launch of the GEMM (FETCH_SIZE + WRITE_SIZE,
+    calibrated on a plain copy), if taken on the current kernel sources."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     t = json.load(open(p))
     if t.get("source_hash") != src_hash:
         return None
-    return t.get("gemm_mxfp4_mlp_bytes_per_launch")
+    k = t.get("kernels", {}).get(GEMM_KERNEL)
+    return None if k is None else k["bytes_per_launch"]
 
 
 def main():
@@ -202,6 +198,7 @@ def main():
     gemm_tf = flops / (res["gemm_ms"] * 1e-3) / 1e12
     a_bytes = M * K * 2 + M * K // 2 + M * K // 32
     w_bytes = N * K * 2 + N * K // 2 + N * K // 32
+    from microscaling_block_scaled_amd.profile_kernels import kernel_source_hash
     src_hash = kernel_source_hash()
     out = {
         "metric": METRIC,
