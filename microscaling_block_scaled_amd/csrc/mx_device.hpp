@@ -55,51 +55,40 @@ __device__ __forceinline__ uint32_t scale_code(uint32_t amax_bits) {
 // ---------------------------------------------------------------------------
 // exact integer conversion of one element, RNE or SR
 // ---------------------------------------------------------------------------
-// `vbits`: fp32 bits of a finite, already-flushed V.  `code`: the block's scale
-// code (not 0xFF).  Computes Q(V / 2^(code-127)) on the element grid with the
-// magnitude rounded to nearest even (SR == false) or rounded up iff
-// r < floor(frac * 2^32) (SR == true), saturating at the largest normal.
+// `vbits`: fp32 bits of a finite V (a subnormal counts as zero, the flush of
+// Algorithm 1).  `code`: the block's scale code (not 0xFF).  Computes
+// Q(V / 2^(code-127)) on the element grid, the magnitude rounded to nearest
+// even (SR == false) or rounded up iff r < floor(frac * 2^32) (SR == true),
+// saturating at the largest normal.
+//
+// With |V| = m * 2^(Ev - 150) and the grid step 2^t of V / X's binade, the
+// magnitude in steps is m / 2^sh; one 64-bit shift (m << 32) >> sh leaves n =
+// floor(m / 2^sh) in the high word and the top 32 bits of the discarded
+// fraction in the low word.  For RNE, sh > 32 means the fraction is below
+// 2^-8, so the low word decides ties exactly.
 template <int F, bool SR>
-__device__ __forceinline__ uint32_t cvt_exact(uint32_t vbits, uint32_t code, uint32_t r) {
+__host__ __device__ __forceinline__ uint32_t cvt_exact(uint32_t vbits, uint32_t code, uint32_t r) {
   using T = Fmt<F>;
   const uint32_t sign = vbits >> 31;
   const uint32_t ab = vbits & 0x7FFFFFFFu;
   const int Ev = (int)(ab >> 23);
-  uint32_t n = 0, up = 0;
-  int e = 0;
-  if (Ev != 0) {
-    const uint32_t m = (ab & 0x7FFFFFu) | 0x800000u;  // |V| = m * 2^(Ev - 150)
-    const int ey = Ev - (int)code;                   // exponent of |V / X|
-    int sh;
-    if (F == INT8) {
-      sh = 17 - ey;  // grid step 2^-6
-    } else {
-      e = ey < T::emin ? T::emin : ey;
-      sh = 23 - T::mbits + (e - ey);
-    }
-    if (sh < 32) {
-      n = m >> sh;
-      if (SR) {
-        const uint32_t F32 = m << (32 - sh);  // discarded fraction, top 32 bits
-        up = r < F32;
-      } else {
-        const uint32_t rem = m & ((1u << sh) - 1u);
-        const uint32_t half = 1u << (sh - 1);
-        up = (rem > half) | ((rem == half) & (n & 1u));
-      }
-    } else {
-      n = 0;
-      if (SR) {
-        const uint32_t F32 = (sh - 32 < 32) ? (m >> (sh - 32)) : 0u;
-        up = r < F32;
-      } else {
-        up = 0;  // |y| < 2^24 * 2^-32 of a step: below half
-      }
-    }
-    n += up;
+  const uint32_t m = Ev ? ((ab & 0x7FFFFFu) | 0x800000u) : 0u;
+  const int ey = Ev ? Ev - (int)code : -1024;  // exponent of |V / X|; zero: below every grid
+  int e = 0, sh;
+  if (F == INT8) {
+    sh = 17 - ey;  // grid step 2^-6
   } else {
-    e = T::emin;
+    e = ey < T::emin ? T::emin : ey;
+    sh = 23 - T::mbits + (e - ey);
   }
+  sh = sh > 63 ? 63 : sh;
+  const uint64_t x = ((uint64_t)m << 32) >> sh;
+  uint32_t n = (uint32_t)(x >> 32);
+  const uint32_t lo = (uint32_t)x;
+  if (SR)
+    n += r < lo ? 1u : 0u;
+  else
+    n += (lo > 0x80000000u || (lo == 0x80000000u && (n & 1u))) ? 1u : 0u;
   if (F == INT8) {
     if (n > 127u) n = 127u;
     return sign ? ((0u - n) & 0xFFu) : n;
@@ -128,9 +117,13 @@ __device__ __forceinline__ U4 philox(uint32_t c0, uint32_t c1, uint32_t c2, uint
                                      uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int i = 0; i < 10; i++) {
-    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
-    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
-    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    // one 32 x 32 -> 64-bit multiply gives both halves (V_MAD_U64_U32), and
+    // one three-input logic op each new word (truth table 0x96: a ^ b ^ c)
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+    const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32(hi1, c1, k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32(hi0, c3, k1, 0x96);
     c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
     k0 += 0x9E3779B9u; k1 += 0xBB67AE85u;
   }

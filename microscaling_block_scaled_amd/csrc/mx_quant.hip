@@ -16,8 +16,8 @@
 //   k_quant_tiles  column-wise layout stored transposed, optionally fused with
 //                  the row-wise one (one HBM read for both).  A 128 x 256 bf16
 //                  tile (128 x 128 fp32) is read with coalesced 16-byte loads,
-//                  row blocks are emitted from registers, the flushed tile is
-//                  staged in LDS, and each lane then owns one 32-row column
+//                  row blocks are emitted from registers, the tile is staged
+//                  in LDS, and each lane then owns one 32-row column
 //                  block of a few columns; four consecutive lanes write 128
 //                  contiguous bytes of a transposed output row.
 #include "mx_device.hpp"
@@ -121,7 +121,7 @@ __device__ __forceinline__ Pack8 convert8(const uint32_t v[8], uint32_t code, co
     return hw_convert8<F>(v, code);
   uint32_t c[8];
 #pragma unroll
-  for (int k = 0; k < 8; k++) c[k] = cvt_exact<F, SR>(daz32(v[k]), code, SR ? rnd[k] : 0u);
+  for (int k = 0; k < 8; k++) c[k] = cvt_exact<F, SR>(v[k], code, SR ? rnd[k] : 0u);
   return pack8<F>(c);
 }
 
@@ -173,12 +173,25 @@ __device__ __forceinline__ void store32(uint8_t* p, const Pack8 o[4]) {
 // ---------------------------------------------------------------------------
 // Block spread over a quad: lane q holds elements 8q .. 8q+7.  Stages with
 // stride 1, 2, 4 are inside the lane, 8 and 16 pair lanes q^1 and q^2.  Each
-// pair (x_j, x_{j+h}) becomes (x_j + x_{j+h}, x_j - x_{j+h}).
-__device__ __forceinline__ void hadamard_quad(uint32_t v[8], int q, uint32_t signs) {
+// pair (x_j, x_{j+h}) becomes (x_j + x_{j+h}, x_j - x_{j+h}): the lane holding
+// x_{j+h} computes x_j + (-x_{j+h}), the same single rounding.  `sw` are the
+// lane's sign masks (bit 31 set where element 8q + k is negated first).
+struct HadLane {
+  uint32_t sw[8];
+  uint32_t flip1, flip2;  // sign bit set on the lanes that subtract in stage 8 / 16
+};
+__device__ __forceinline__ HadLane had_lane(uint32_t signs, int q) {
+  HadLane h;
+#pragma unroll
+  for (int k = 0; k < 8; k++) h.sw[k] = ((signs >> (8 * q + k)) & 1u) << 31;
+  h.flip1 = (uint32_t)(q & 1) << 31;
+  h.flip2 = (uint32_t)(q & 2) << 30;
+  return h;
+}
+__device__ __forceinline__ void hadamard_quad(uint32_t v[8], const HadLane& hl) {
   float f[8];
 #pragma unroll
-  for (int k = 0; k < 8; k++)
-    f[k] = __builtin_bit_cast(float, v[k] ^ (((signs >> (8 * q + k)) & 1u) << 31));
+  for (int k = 0; k < 8; k++) f[k] = __builtin_bit_cast(float, v[k] ^ hl.sw[k]);
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
@@ -192,12 +205,12 @@ __device__ __forceinline__ void hadamard_quad(uint32_t v[8], int q, uint32_t sig
 #pragma unroll
   for (int k = 0; k < 8; k++) {
     const float o = quad_xor1f(f[k]);
-    f[k] = (q & 1) ? (o - f[k]) : (f[k] + o);
+    f[k] = o + __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, f[k]) ^ hl.flip1);
   }
 #pragma unroll
   for (int k = 0; k < 8; k++) {
     const float o = quad_xor2f(f[k]);
-    f[k] = (q & 2) ? (o - f[k]) : (f[k] + o);
+    f[k] = o + __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, f[k]) ^ hl.flip2);
   }
   const float c = inv_sqrt32();
 #pragma unroll
@@ -259,16 +272,19 @@ __device__ __forceinline__ void widen8(const uint32_t* raw, uint32_t v[8]) {
 
 // Quantize the 8 elements v (fp32 bits) at row r, chunk c (elements 8c..8c+7)
 // into the row-wise layout.  The four lanes of the block are one DPP quad, q =
-// c & 3 is this lane's place in it.  All four lanes must be active.
+// c & 3 is this lane's place in it (the same for every chunk of a lane; `hl`
+// holds its Hadamard constants).  All four lanes must be active.  Inputs are
+// flushed before the transform; after it no flush is needed: a subnormal
+// block maximum gives scale code 0 either way, and the conversions treat a
+// subnormal element as zero.
 template <int F, bool SR, bool HAD>
-__device__ __forceinline__ void row_chunk(const QP& p, int64_t r, int64_t c, uint32_t v[8]) {
+__device__ __forceinline__ void row_chunk(const QP& p, int64_t r, int64_t c, uint32_t v[8],
+                                          const HadLane& hl) {
   const int q = (int)(c & 3);
   if (HAD) {
 #pragma unroll
     for (int k = 0; k < 8; k++) v[k] = daz32(v[k]);
-    hadamard_quad(v, q, p.signs);
-#pragma unroll
-    for (int k = 0; k < 8; k++) v[k] = daz32(v[k]);
+    hadamard_quad(v, hl);
   }
   uint32_t am = 0;
 #pragma unroll
@@ -312,6 +328,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(QP p) {
   const int lpr = 1 << p.lpr_log2;
   const int tid = threadIdx.x;
   const int lr = tid & (lpr - 1);
+  const HadLane hl = had_lane(p.signs, lr & 3);  // chunk c = lr + k lpr: c & 3 == lr & 3
   const int rpp = 256 >> p.lpr_log2;
   const int64_t cpr = p.cols >> 3;  // 8-element chunks per row
   const int64_t r0 = (int64_t)blockIdx.x * p.rows_per_block;
@@ -328,7 +345,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(QP p) {
         if (c + u * lpr < cpr) {
           uint32_t v[8];
           widen8<SRC>(raw[u], v);
-          row_chunk<F, SR, HAD>(p, r, c + u * lpr, v);
+          row_chunk<F, SR, HAD>(p, r, c + u * lpr, v, hl);
         }
       }
     }
@@ -356,8 +373,6 @@ __device__ __forceinline__ void col_block(const QP& p, uint32_t v[32], int64_t c
 #pragma unroll
     for (int k = 0; k < 32; k++) v[k] = daz32(v[k]);
     hadamard_local(v, p.signs);
-#pragma unroll
-    for (int k = 0; k < 32; k++) v[k] = daz32(v[k]);
   }
   uint32_t am = 0;
 #pragma unroll
@@ -392,6 +407,7 @@ __global__ __launch_bounds__(256) void k_quant_tiles(QP p) {
   const int tr_eff = (int)(p.rows - r0 < T::TR ? p.rows - r0 : T::TR);
   const int tc_eff = (int)(p.cols - c0 < T::TC ? p.cols - c0 : T::TC);
   const int cq = tid % T::CPRW, sub = tid / T::CPRW;
+  const HadLane hl = had_lane(p.signs, cq & 3);  // tile columns start at a multiple of 4 chunks
   const bool col_ok = cq * 8 < tc_eff;
 
   uint32_t raw[T::PASSES][T::RAWN];
@@ -421,18 +437,14 @@ __global__ __launch_bounds__(256) void k_quant_tiles(QP p) {
         uint32_t w[8];
 #pragma unroll
         for (int k = 0; k < 8; k++) w[k] = v[k];
-        row_chunk<F, SR, HAD>(p, r0 + row, (c0 >> 3) + cq, w);
+        row_chunk<F, SR, HAD>(p, r0 + row, (c0 >> 3) + cq, w, hl);
       }
       uint8_t* dst = lds + row * T::PITCH + cq * 8 * T::ESZ;
       if (SRC == SRC_BF16) {
-        uint32_t d[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-          d[i] = (daz32(v[2 * i]) >> 16) | (daz32(v[2 * i + 1]) & 0xFFFF0000u);
-        *(uint4*)dst = make_uint4(d[0], d[1], d[2], d[3]);
+        *(uint4*)dst = make_uint4(raw[pp][0], raw[pp][1], raw[pp][2], raw[pp][3]);
       } else {
-        *(uint4*)dst = make_uint4(daz32(v[0]), daz32(v[1]), daz32(v[2]), daz32(v[3]));
-        *(uint4*)(dst + 16) = make_uint4(daz32(v[4]), daz32(v[5]), daz32(v[6]), daz32(v[7]));
+        *(uint4*)dst = make_uint4(v[0], v[1], v[2], v[3]);
+        *(uint4*)(dst + 16) = make_uint4(v[4], v[5], v[6], v[7]);
       }
     }
   }
