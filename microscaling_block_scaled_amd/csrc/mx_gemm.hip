@@ -22,6 +22,8 @@
 //   FP6 (E2M3, E3M2): the 24 packed bytes of block kb
 //   FP4 (E2M1):       the 16 packed bytes of block kb
 // Result: lane l holds C rows 4 (l / 16) + v, v = 0..3, column l % 16.
+#include <utility>
+
 #include "mx_device.hpp"
 #include "mx_internal.h"
 
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ aq,
 // ---------------------------------------------------------------------------
 // fast path (K % 512 == 0, scale arrays 16-byte aligned, operands < 4 GiB)
 //
-// A 512-thread workgroup computes a 256 x 256 tile of C.  Per stage of KS
+// A 256-thread workgroup computes a 256 x 256 tile of C.  Per stage of KS
 // elements of K (256 when both operands are FP4, so that every operand row of
 // a stage is one 128-byte line; else 128) the A and B panels (256 rows each)
 // go global -> LDS directly (buffer_load ... lds; rows past the matrix edge
@@ -229,13 +231,13 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ aq,
 // row at a time, into two alternating LDS buffers: one 16-byte load per lane
 // pair and row instead of a few bytes per row and stage.
 //
-// The eight waves own 128 x 64 pieces of the tile and form two groups of four
-// (one wave of each group per SIMD) that alternate roles every phase: while
-// group 0 issues the matrix instructions of one 64-element substep, group 1
-// reads its operands of that substep from LDS, and the other way round in the
-// next phase.  So on every SIMD one wave feeds the matrix unit while the other
-// moves data.  B is passed as the instruction's first operand so that a
-// lane's results are four consecutive columns of C (16-byte stores).
+// Four waves own 128 x 128 pieces of the tile, with their accumulators in the
+// AGPR file.  A stage is SUB substeps of 64 elements of K (one
+// V_MFMA_SCALE_F32_32X32X64_F8F6F4 deep); each wave issues a substep's 16
+// instructions with the LDS reads of the next substep's operands slotted in
+// between them (double-buffered operand registers), so the matrix unit is
+// fed while the next operands arrive.  One barrier per stage, before its last
+// substep, hands the ring slot back to the loads.
 // ---------------------------------------------------------------------------
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -257,10 +259,6 @@ template <int FA, int FB, int KS_> struct Fast {
   static constexpr int NST = NST0 > 4 ? 4 : NST0;
   static constexpr int SC_OFF = NST * STAGE;
   static constexpr int TOTAL = SC_OFF + 2 * SC_BUF;
-  // 1 KB panel segments per stage (4 (CHA + CHB)), shared out over 8 waves
-  static constexpr int SEG_A = 4 * CHA;
-  static constexpr int SEGS = (CHA + CHB) / 2;
-  static_assert((CHA + CHB) % 2 == 0, "panel segments split evenly over 8 waves");
   static_assert(NST >= 2 && SPC >= NST, "stage ring and scale buffers");
 };
 
@@ -380,52 +378,92 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
   tn = w / gm;
 }
 
-// Operands of one substep for one wave: 4 A tiles and 2 B tiles of 32 rows.
+// Operands of one 64-element substep for one wave: 4 A tiles and 4 B tiles of
+// 32 rows, with their scale bytes.
 struct Ops {
-  v8i a[4], b[2];
-  int sa[4], sb[2];
+  v8i a[4], b[4];
+  int sa[4], sb[4];
 };
 
 // Where a wave's operands sit in LDS: its rows' offsets and swizzles.
 struct Lanes {
   int arow, brow;  // first A / B row of the wave's tiles for this lane
   int kb, swa, swb;
+  int bsh[2];      // bit offset of the lane's scale byte in a word, even / odd substep
 };
 
-// Operands of substep u of stage s.
+// The scale bytes of one stage for the wave's 8 tiles: KS / 32 bytes per row
+// (one or two dwords), read once per stage.
+template <int KS> struct ScaleWords {
+  uint32_t a[4][KS / 128], b[4][KS / 128];
+};
+
 template <class C, int FA, int FB>
-__device__ __forceinline__ void read_ops(Ops& o, const uint8_t* lds, int s, int u, const Lanes& w) {
-  const uint8_t* st = lds + (s % C::NST) * C::STAGE;
-  const uint8_t* la = st + C::A_OFF + w.arow * C::RBA;
-  const uint8_t* lb = st + C::B_OFF + w.brow * C::RBB;
-  const uint8_t* sc = lds + C::SC_OFF + ((s / C::SPC) & 1) * C::SC_BUF +
-                      (s % C::SPC) * (C::KS / 32) + 2 * u + w.kb;
-  const uint8_t* sa = sc + w.arow * C::SC_ROW;
-  const uint8_t* sb = sc + (256 + w.brow) * C::SC_ROW;
-#pragma unroll
-  for (int j = 0; j < 2; j++) {
-    o.b[j] = read32<FB, C::CHB>(lb, j * 32 * C::RBB, u, w.kb, w.swb);
-    o.sb[j] = sb[j * 32 * C::SC_ROW];
-  }
+__device__ __forceinline__ void read_scale_words(ScaleWords<C::KS>& sw, const uint8_t* lds, int s,
+                                                 const Lanes& w) {
+  const uint8_t* sc = lds + C::SC_OFF + ((s / C::SPC) & 1) * C::SC_BUF + (s % C::SPC) * (C::KS / 32);
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    o.a[i] = read32<FA, C::CHA>(la, i * 32 * C::RBA, u, w.kb, w.swa);
-    o.sa[i] = sa[i * 32 * C::SC_ROW];
+    const uint8_t* pa = sc + (w.arow + 32 * i) * C::SC_ROW;
+    const uint8_t* pb = sc + (256 + w.brow + 32 * i) * C::SC_ROW;
+    if (C::KS == 256) {
+      const uint2 x = *(const uint2*)pa, y = *(const uint2*)pb;
+      sw.a[i][0] = x.x; sw.a[i][C::KS / 128 - 1] = x.y;
+      sw.b[i][0] = y.x; sw.b[i][C::KS / 128 - 1] = y.y;
+    } else {
+      sw.a[i][0] = *(const uint32_t*)pa;
+      sw.b[i][0] = *(const uint32_t*)pb;
+    }
   }
 }
 
-template <int FA, int FB>
-__device__ __forceinline__ void mma_ops(v16f (&acc)[4][2], const Ops& o) {
+// Scale operands of substep u: byte 2u + kb of the stage's bytes of the row.
+template <int KS>
+__device__ __forceinline__ void scales_of(Ops& o, const ScaleWords<KS>& sw, int u, const Lanes& w) {
 #pragma unroll
-  for (int i = 0; i < 4; i++)
-#pragma unroll
-    for (int j = 0; j < 2; j++)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.b[j], o.a[i], acc[i][j], FB, FA,
-                                                                  0, o.sb[j], 0, o.sa[i]);
+  for (int i = 0; i < 4; i++) {
+    o.sa[i] = (int)__builtin_amdgcn_ubfe(sw.a[i][u / 2], w.bsh[u & 1], 8);
+    o.sb[i] = (int)__builtin_amdgcn_ubfe(sw.b[i][u / 2], w.bsh[u & 1], 8);
+  }
+}
+
+// One tile's operand of substep u (t < 4: A tile t, else B tile t - 4).
+template <class C, int FA, int FB>
+__device__ __forceinline__ void read_tile(Ops& o, const uint8_t* st, int u, int t, const Lanes& w) {
+  if (t < 4)
+    o.a[t] = read32<FA, C::CHA>(st + C::A_OFF + (w.arow + 32 * t) * C::RBA, 0, u, w.kb, w.swa);
+  else
+    o.b[t - 4] = read32<FB, C::CHB>(st + C::B_OFF + (w.brow + 32 * (t - 4)) * C::RBB, 0, u, w.kb, w.swb);
+}
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1: a loop whose index
+// is a compile-time constant in the body however large the body is.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// One substep: the 16 block-scaled instructions on `cur`, each followed by
+// `slot(k)` (LDS reads of the next substep's operands, the barrier, loads),
+// in exactly this order (scheduling fences).  B is the instruction's first
+// operand, so a lane's results are four consecutive columns of C.
+template <int FA, int FB, class Slot>
+__device__ __forceinline__ void substep(v16f (&acc)[4][4], const Ops& cur, Slot&& slot) {
+  static_for<16>([&](auto K) {
+    constexpr int k = decltype(K)::value, i = k >> 2, j = k & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.b[j], cur.a[i], acc[i][j], FB, FA,
+                                                                0, cur.sb[j], 0, cur.sa[i]);
+    slot(K);
+    __builtin_amdgcn_sched_barrier(0);
+  });
 }
 
 template <int FA, int FB, int KS>
-__global__ __launch_bounds__(512) void k_gemm_fast(const uint8_t* __restrict__ aq,
+__global__ __launch_bounds__(256) void k_gemm_fast(const uint8_t* __restrict__ aq,
                                                    const uint8_t* __restrict__ as,
                                                    const uint8_t* __restrict__ bq,
                                                    const uint8_t* __restrict__ bs, int64_t M,
@@ -434,12 +472,17 @@ __global__ __launch_bounds__(512) void k_gemm_fast(const uint8_t* __restrict__ a
                                                    int vec_store) {
   using C = Fast<FA, FB, KS>;
   constexpr int NST = C::NST, SUB = C::SUB, SPC = C::SPC;
+  constexpr int SEGS = C::CHA + C::CHB;  // 1 KB panel segments per wave per stage
+  constexpr int SEG_A = 4 * C::CHA;
+  // An accumulation-register operand anywhere in the kernel lets the compiler
+  // place the accumulators in the AGPR file (256 of them per wave), leaving
+  // the VGPRs to two substeps of operands.
+  asm volatile("; uses agprs %0" : : "a"(0));
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::TOTAL];
   const int tid = threadIdx.x, lane = tid & 63;
   // wave index as a wave-uniform (scalar) value: LDS destinations stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool g1 = wave >= 4;                // role group
-  const int wm = wave & 1, wn = wave >> 1;  // 2 x 4 pieces of 128 x 64
+  const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 pieces of 128 x 128
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
@@ -447,18 +490,18 @@ __global__ __launch_bounds__(512) void k_gemm_fast(const uint8_t* __restrict__ a
   const int64_t nblk = K / 32;
   const int nk = (int)(K / KS);
 
-  // this wave's panel segments I = wave + 8 k (A segments first, then B);
+  // this wave's panel segments I = wave + 4 k (A segments first, then B);
   // lane chunk I * 64 + lane of the panel
   const v4i ra = make_rsrc(aq, (uint32_t)(M * arow));
   const v4i rb = make_rsrc(bq, (uint32_t)(N * brow));
-  uint32_t voff[C::SEGS];
-  uint32_t lofs[C::SEGS];
-  bool isb[C::SEGS];
+  uint32_t voff[SEGS];
+  uint32_t lofs[SEGS];
+  bool isb[SEGS];
 #pragma unroll
-  for (int k = 0; k < C::SEGS; k++) {
-    const int I = wave + 8 * k;
-    isb[k] = I >= C::SEG_A;
-    const int Ip = isb[k] ? I - C::SEG_A : I;
+  for (int k = 0; k < SEGS; k++) {
+    const int I = wave + 4 * k;
+    isb[k] = I >= SEG_A;
+    const int Ip = isb[k] ? I - SEG_A : I;
     const int ch = isb[k] ? C::CHB : C::CHA;
     const int Lc = Ip * 64 + lane;
     const int r = Lc / ch, pc = Lc % ch;
@@ -466,12 +509,14 @@ __global__ __launch_bounds__(512) void k_gemm_fast(const uint8_t* __restrict__ a
     voff[k] = isb[k] ? (uint32_t)((n0 + r) * brow + 16 * cc) : (uint32_t)((m0 + r) * arow + 16 * cc);
     lofs[k] = (uint32_t)((isb[k] ? C::B_OFF : C::A_OFF) + Ip * 1024);
   }
-  // scale chunks: wave w loads A scale rows 32 w .. 32 w + 31 and the same B
-  // rows, lane pair (2 r, 2 r + 1) the two 16-byte halves of row r's 32 bytes
+  // scale chunks: wave w loads A scale rows 64 w .. 64 w + 63 and the same B
+  // rows, 32 rows per load, lane pair (2 r, 2 r + 1) the two 16-byte halves of
+  // row r's 32 bytes
   const v4i rsa = make_rsrc(as, (uint32_t)(M * nblk));
   const v4i rsb = make_rsrc(bs, (uint32_t)(N * nblk));
-  const uint32_t vsa = (uint32_t)((m0 + wave * 32 + (lane >> 1)) * nblk + 16 * (lane & 1));
-  const uint32_t vsb = (uint32_t)((n0 + wave * 32 + (lane >> 1)) * nblk + 16 * (lane & 1));
+  const uint32_t vsa = (uint32_t)((m0 + wave * 64 + (lane >> 1)) * nblk + 16 * (lane & 1));
+  const uint32_t vsb = (uint32_t)((n0 + wave * 64 + (lane >> 1)) * nblk + 16 * (lane & 1));
+  const uint32_t half_rows = (uint32_t)(32 * nblk);
   const uint32_t lds0 = lds_addr(lds);
   // Stage s into ring slot s % NST, preceded (first stage of a chunk) by the
   // scale chunk s / SPC into scale buffer (s / SPC) % 2.  The scale loads are
@@ -480,16 +525,20 @@ __global__ __launch_bounds__(512) void k_gemm_fast(const uint8_t* __restrict__ a
   // an empty buffer resource: every lane reads out of range, which fetches
   // nothing, and the slot it fills is not read again.
   const v4i rnone = {0, 0, 0, 0x00020000};
-  auto issue = [&](int s) {
+  // load j (0 .. NLD-1) of stage s: the four scale loads, then the panel
+  // segments
+  constexpr int NLD = 4 + SEGS;
+  auto issue_one = [&](int s, int j) {
     const bool live = s < nk;
-    const bool chunk = live && (s % SPC) == 0;
-    const uint32_t sdst = lds0 + C::SC_OFF + ((s / SPC) & 1) * C::SC_BUF + wave * 1024;
-    const uint32_t soff = chunk ? (uint32_t)(s / SPC) * C::SC_ROW : 0u;
-    dma16_if(rsa, vsa, soff, sdst, chunk);
-    dma16_if(rsb, vsb, soff, sdst + 256 * C::SC_ROW, chunk);
-    const uint32_t st = lds0 + (uint32_t)((s % NST) * C::STAGE);
-#pragma unroll
-    for (int k = 0; k < C::SEGS; k++) {
+    if (j < 4) {
+      const bool chunk = live && (s % SPC) == 0;
+      const uint32_t sdst = lds0 + C::SC_OFF + ((s / SPC) & 1) * C::SC_BUF + wave * 64 * C::SC_ROW +
+                            (j >> 1) * 256 * C::SC_ROW + (j & 1) * 32 * C::SC_ROW;
+      const uint32_t soff = chunk ? (uint32_t)(s / SPC) * C::SC_ROW + (j & 1) * half_rows : 0u;
+      dma16_if(j < 2 ? rsa : rsb, j < 2 ? vsa : vsb, soff, sdst, chunk);
+    } else {
+      const int k = j - 4;
+      const uint32_t st = lds0 + (uint32_t)((s % NST) * C::STAGE);
       const uint32_t kb0 = live ? (uint32_t)s * (isb[k] ? C::RBB : C::RBA) : 0u;
       dma16(live ? (isb[k] ? rb : ra) : rnone, voff[k], kb0, st + lofs[k]);
     }
@@ -500,89 +549,92 @@ __global__ __launch_bounds__(512) void k_gemm_fast(const uint8_t* __restrict__ a
     const int lr = lane & 31;
     w.kb = lane >> 5;
     w.arow = wm * 128 + lr;
-    w.brow = wn * 64 + lr;
+    w.brow = wn * 128 + lr;
     w.swa = swz<C::CHA>(lr);
     w.swb = swz<C::CHB>(lr);
+    w.bsh[0] = 8 * w.kb;
+    w.bsh[1] = 16 + 8 * w.kb;
   }
 
-  v16f acc[4][2];
+  v16f acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 2; j++)
+    for (int j = 0; j < 4; j++)
 #pragma unroll
       for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
-  Ops ops;
+  Ops ops[2];
+  ScaleWords<KS> sw;
+  auto slot = [&](int s) { return lds + (s % NST) * C::STAGE; };
 
   // prologue: stages 0 .. NST-1 in flight, wait for stage 0 (a wait counts
   // panel loads only: masked-off scale loads may or may not count, and where
-  // they do the wait is merely longer)
+  // they do the wait is merely longer), then substep (0, 0)'s operands
 #pragma unroll
-  for (int i = 0; i < NST; i++) issue(i);
+  for (int i = 0; i < NST; i++)
+#pragma unroll
+    for (int j = 0; j < NLD; j++) issue_one(i, j);
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"((NST - 1) * C::SEGS) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"((NST - 1) * SEGS) : "memory");
   __builtin_amdgcn_sched_barrier(0);
-  // 2 SUB phases per stage s, separated by barriers; the two groups run the
-  // same barrier sequence in separate loops.  In phase 2j group 0 computes
-  // substep (s, j) while group 1 reads it; in phase 2j + 1 group 1 computes
-  // (s, j) while group 0 reads (s, j + 1), and the last phase, which starts
-  // with the wait for stage s + 1 (this wave's loads of it landed, its own
-  // LDS reads back, then the barrier: every wave is done with slot s % NST),
-  // refills that slot with stage s + NST while group 0 reads (s + 1, 0).
-  // Every phase is unconditional, so each loop body is one basic block and
-  // the scheduling fences at the barriers keep each phase's instructions in
-  // place.  Group 0's loop runs from that last phase of stage s to the end of
-  // stage s + 1, so that no operand register lives across iterations.
-  constexpr int AHEAD = (NST - 2) * C::SEGS;  // panel loads still in flight at a wait
-  if (!g1) {
-    read_ops<C, FA, FB>(ops, lds, 0, 0, w);
+  read_scale_words<C, FA, FB>(sw, lds, 0, w);
+  scales_of<KS>(ops[0], sw, 0, w);
 #pragma unroll
-    for (int u = 0; u < SUB; u++) {
-      barrier();
-      mma_ops<FA, FB>(acc, ops);
-      if (u + 1 < SUB) {
-        barrier();
-        read_ops<C, FA, FB>(ops, lds, 0, u + 1, w);
-      }
-    }
-    for (int s = 0; s + 1 < nk; s++) {
-      wait_all_barrier<AHEAD>();
-      read_ops<C, FA, FB>(ops, lds, s + 1, 0, w);
-      issue(s + NST);
-#pragma unroll
-      for (int u = 0; u < SUB; u++) {
-        barrier();
-        mma_ops<FA, FB>(acc, ops);
-        if (u + 1 < SUB) {
-          barrier();
-          read_ops<C, FA, FB>(ops, lds, s + 1, u + 1, w);
+  for (int t = 0; t < 8; t++) read_tile<C, FA, FB>(ops[0], slot(0), 0, t, w);
+
+  // Per stage: SUB substeps.  Substep u's instructions run on ops[u % 2] while
+  // the next substep's operands are read into ops[(u + 1) % 2], one tile after
+  // each of instructions 0-7.  Once the last substep's operands are in (after
+  // instruction SK of substep SU), every wave waits for stage s + 1 (its own
+  // loads of it landed, its LDS reads back, then the barrier: every wave is
+  // also done reading slot s % NST) and reads stage s + 1's scale words; the
+  // loads of stage s + NST into that slot are then spread over the remaining
+  // instruction slots of the stage, and the last substep reads (s + 1, 0).
+  // The loop body is one basic block; in the last stage the operands read for
+  // stage nk are never used.
+  constexpr int AHEAD = (NST - 2) * SEGS;  // panel loads still in flight at a wait
+  constexpr int SU = SUB >= 4 ? SUB - 2 : SUB - 1;
+  constexpr int SK = SUB >= 4 ? 11 : 3;
+  constexpr int NSLOT = (15 - SK) + 16 * (SUB - 1 - SU);  // slots after the wait
+  ScaleWords<KS> swn;
+  for (int s = 0; s < nk; s++) {
+    static_for<SUB>([&](auto U) {
+      constexpr int u = decltype(U)::value;
+      constexpr bool last = u == SUB - 1;
+      Ops& nxt = ops[(u + 1) & 1];
+      const uint8_t* st = last ? slot(s + 1) : slot(s);
+      substep<FA, FB>(acc, ops[u & 1], [&](auto K) {
+        constexpr int k = decltype(K)::value;
+        if constexpr (u == SU && k == SK) {
+          wait_all_barrier<AHEAD>();
+          read_scale_words<C, FA, FB>(swn, lds, s + 1, w);
         }
-      }
-    }
-    wait_all_barrier<AHEAD>();  // pairs with group 1's last wait
-  } else {
-    for (int s = 0; s < nk; s++) {
-#pragma unroll
-      for (int u = 0; u < SUB; u++) {
-        barrier();
-        read_ops<C, FA, FB>(ops, lds, s, u, w);
-        if (u + 1 < SUB) {
-          barrier();
-          mma_ops<FA, FB>(acc, ops);
+        // the last substep's reads follow the wait when it falls in that substep
+        constexpr int r0 = (last && SU == SUB - 1) ? SK + 1 : 0;
+        if constexpr (k >= r0 && k < r0 + 8) read_tile<C, FA, FB>(nxt, st, last ? 0 : u + 1, k - r0, w);
+        constexpr int g = (u - SU) * 16 + (k - SK - 1);  // slot index after the wait
+        if constexpr (g >= 0 && g < NSLOT) {
+          static_for<NLD>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            if constexpr ((j * NSLOT) / NLD == g) issue_one(s + NST, j);
+          });
         }
+      });
+      if constexpr (last) {
+        scales_of<KS>(nxt, swn, 0, w);
+        sw = swn;
+      } else {
+        scales_of<KS>(nxt, sw, u + 1, w);
       }
-      wait_all_barrier<AHEAD>();
-      issue(s + NST);
-      mma_ops<FA, FB>(acc, ops);
-    }
+    });
   }
   // the out-of-range loads of the last stages must be done before the
   // workgroup's LDS is released
   asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
 
   // acc[i][j] is the 32 x 32 tile C^T[n][m]: lane l holds, for v = 4q + e,
-  // C[m0 + wm*128 + 32 i + l % 32][n0 + wn*64 + 32 j + 8 q + 4 (l / 32) + e]
+  // C[m0 + wm*128 + 32 i + l % 32][n0 + wn*128 + 32 j + 8 q + 4 (l / 32) + e]
   const int lr = lane & 31;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
@@ -590,10 +642,10 @@ __global__ __launch_bounds__(512) void k_gemm_fast(const uint8_t* __restrict__ a
     if (row >= M) continue;
     float* crow = c + row * ldc;
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
+    for (int j = 0; j < 4; j++) {
 #pragma unroll
       for (int q = 0; q < 4; q++) {
-        const int64_t col = n0 + wn * 64 + j * 32 + 8 * q + 4 * w.kb;
+        const int64_t col = n0 + wn * 128 + j * 32 + 8 * q + 4 * w.kb;
         const v16f& tt = acc[i][j];
         if (vec_store && col + 3 < N) {
           *(float4*)(crow + col) = make_float4(tt[4 * q], tt[4 * q + 1], tt[4 * q + 2], tt[4 * q + 3]);
@@ -612,7 +664,7 @@ static hipError_t launch_fast(const void* aq, const uint8_t* as, const void* bq,
                               int64_t M, int64_t N, int64_t K, float* c, int64_t ldc,
                               int64_t tiles_m, int64_t tiles_n, hipStream_t st) {
   const int vec = ((uintptr_t)c % 16) == 0 && ldc % 4 == 0;
-  hipLaunchKernelGGL((k_gemm_fast<FA, FB, KS>), dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0,
+  hipLaunchKernelGGL((k_gemm_fast<FA, FB, KS>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
                      st, (const uint8_t*)aq, as, (const uint8_t*)bq, bs, M, N, K, c, ldc,
                      (int)tiles_m, (int)tiles_n, vec);
   return hipGetLastError();
