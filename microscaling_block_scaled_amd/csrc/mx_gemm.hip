@@ -234,10 +234,11 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ aq,
 // Four waves own 128 x 128 pieces of the tile, with their accumulators in the
 // AGPR file.  A stage is SUB substeps of 64 elements of K (one
 // V_MFMA_SCALE_F32_32X32X64_F8F6F4 deep); each wave issues a substep's 16
-// instructions with the LDS reads of the next substep's operands slotted in
-// between them (double-buffered operand registers), so the matrix unit is
-// fed while the next operands arrive.  One barrier per stage, before its last
-// substep, hands the ring slot back to the loads.
+// instructions with the LDS reads of a later substep's operands slotted in
+// between them (a ring of operand registers), so the matrix unit is fed
+// while those operands arrive.  One barrier per stage, as soon as the stage's
+// operands are all read, hands the ring slot back to the loads, which are
+// then spread over the rest of the stage.
 // ---------------------------------------------------------------------------
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -564,7 +565,12 @@ __global__ __launch_bounds__(256) void k_gemm_fast(const uint8_t* __restrict__ a
 #pragma unroll
       for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
-  Ops ops[2];
+  // operands are read RA substeps ahead into a ring of NB register sets (NB
+  // divides SUB, so the ring position of a substep is the same every stage)
+  constexpr int RA = SUB >= 4 ? 2 : 1;
+  constexpr int NB = SUB >= 4 ? 4 : 2;
+  static_assert(SUB % NB == 0 && RA < NB, "operand register ring");
+  Ops ops[NB];
   ScaleWords<KS> sw;
   auto slot = [&](int s) { return lds + (s % NST) * C::STAGE; };
 
@@ -579,40 +585,42 @@ __global__ __launch_bounds__(256) void k_gemm_fast(const uint8_t* __restrict__ a
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"((NST - 1) * SEGS) : "memory");
   __builtin_amdgcn_sched_barrier(0);
   read_scale_words<C, FA, FB>(sw, lds, 0, w);
-  scales_of<KS>(ops[0], sw, 0, w);
+  static_for<RA>([&](auto R) {
+    constexpr int r = decltype(R)::value;
+    scales_of<KS>(ops[r], sw, r, w);
 #pragma unroll
-  for (int t = 0; t < 8; t++) read_tile<C, FA, FB>(ops[0], slot(0), 0, t, w);
+    for (int t = 0; t < 8; t++) read_tile<C, FA, FB>(ops[r], slot(0), r, t, w);
+  });
 
-  // Per stage: SUB substeps.  Substep u's instructions run on ops[u % 2] while
-  // the next substep's operands are read into ops[(u + 1) % 2], one tile after
-  // each of instructions 0-7.  Once the last substep's operands are in (after
-  // instruction SK of substep SU), every wave waits for stage s + 1 (its own
-  // loads of it landed, its LDS reads back, then the barrier: every wave is
-  // also done reading slot s % NST) and reads stage s + 1's scale words; the
-  // loads of stage s + NST into that slot are then spread over the remaining
-  // instruction slots of the stage, and the last substep reads (s + 1, 0).
-  // The loop body is one basic block; in the last stage the operands read for
-  // stage nk are never used.
+  // Per stage: SUB substeps.  Substep u's instructions run on ops[u % NB]
+  // while the operands of the substep RA later are read into ops[(u + RA) %
+  // NB], one tile after each of instructions 0-7.  Once the last operands of
+  // stage s are in (after instruction SK of substep SU), every wave waits for
+  // stage s + 1 (its own loads of it landed, its LDS reads back, then the
+  // barrier: every wave is also done reading slot s % NST) and reads stage
+  // s + 1's scale words; the loads of stage s + NST into that slot are then
+  // spread over the remaining instruction slots of the stage, while the last
+  // RA substeps read stage s + 1's first operands.  The loop body is one basic
+  // block; in the last stage the operands read for stage nk are never used.
   constexpr int AHEAD = (NST - 2) * SEGS;  // panel loads still in flight at a wait
-  constexpr int SU = SUB >= 4 ? SUB - 2 : SUB - 1;
-  constexpr int SK = SUB >= 4 ? 11 : 3;
+  constexpr int SU = SUB - 1 - RA;
+  constexpr int SK = 11;
   constexpr int NSLOT = (15 - SK) + 16 * (SUB - 1 - SU);  // slots after the wait
   ScaleWords<KS> swn;
   for (int s = 0; s < nk; s++) {
     static_for<SUB>([&](auto U) {
       constexpr int u = decltype(U)::value;
-      constexpr bool last = u == SUB - 1;
-      Ops& nxt = ops[(u + 1) & 1];
-      const uint8_t* st = last ? slot(s + 1) : slot(s);
-      substep<FA, FB>(acc, ops[u & 1], [&](auto K) {
+      constexpr int un = (u + RA) % SUB;     // substep whose operands are read
+      constexpr bool next = u + RA >= SUB;   // ... of stage s + 1
+      Ops& nxt = ops[(u + RA) % NB];
+      const uint8_t* st = next ? slot(s + 1) : slot(s);
+      substep<FA, FB>(acc, ops[u % NB], [&](auto K) {
         constexpr int k = decltype(K)::value;
         if constexpr (u == SU && k == SK) {
           wait_all_barrier<AHEAD>();
           read_scale_words<C, FA, FB>(swn, lds, s + 1, w);
         }
-        // the last substep's reads follow the wait when it falls in that substep
-        constexpr int r0 = (last && SU == SUB - 1) ? SK + 1 : 0;
-        if constexpr (k >= r0 && k < r0 + 8) read_tile<C, FA, FB>(nxt, st, last ? 0 : u + 1, k - r0, w);
+        if constexpr (k < 8) read_tile<C, FA, FB>(nxt, st, un, k, w);
         constexpr int g = (u - SU) * 16 + (k - SK - 1);  // slot index after the wait
         if constexpr (g >= 0 && g < NSLOT) {
           static_for<NLD>([&](auto J) {
@@ -621,13 +629,12 @@ __global__ __launch_bounds__(256) void k_gemm_fast(const uint8_t* __restrict__ a
           });
         }
       });
-      if constexpr (last) {
-        scales_of<KS>(nxt, swn, 0, w);
-        sw = swn;
-      } else {
-        scales_of<KS>(nxt, sw, u + 1, w);
-      }
+      if constexpr (next)
+        scales_of<KS>(nxt, swn, un, w);
+      else
+        scales_of<KS>(nxt, sw, un, w);
     });
+    sw = swn;
   }
   // the out-of-range loads of the last stages must be done before the
   // workgroup's LDS is released
