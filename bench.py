@@ -35,18 +35,24 @@ def dev_bf16(a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def timed_events(fn, n, stream):
-    """Average duration (ms) of fn() over n launches, HIP events on `stream`."""
+def timed_events(fn, n, stream, batches=5):
+    """Per-launch duration (ms) of fn(): HIP events on `stream` around batches
+    of n back-to-back launches (so no event sits between two launches);
+    returns the median and the mean over the batches of batch time / n."""
     import torch
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
-    evs[0].record(stream)
-    for i in range(n):
-        fn(i)
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    d = [evs[i].elapsed_time(evs[i + 1]) for i in range(n)]
-    d.sort()
-    return d[len(d) // 2], sum(d) / len(d)
+    per = []
+    k = 0
+    for _ in range(batches):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn(k)
+            k += 1
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / n)
+    per.sort()
+    return per[len(per) // 2], sum(per) / len(per)
 
 
 def bench_step(mx, steps, warmup):
@@ -108,7 +114,7 @@ def bench_quant(mx, name, x_host, fmt, layouts, rounds=60):
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
     med, avg = timed_events(lambda i: mx.quantize(xs[i % nsets], fmt, layouts, out=outs[i % nsets]),
-                            rounds, st)
+                            max(rounds // 5, 4), st)
     gbs = (in_bytes + out_bytes) / (med * 1e-3) / 1e9
     del xs, outs
     torch.cuda.empty_cache()
@@ -126,7 +132,7 @@ def bench_gemm(mx, name, a_host, w_host, fa, fw, peak, rounds=20):
     run = lambda i: mx.gemm(qa["q_row"], qa["s_row"], fa, qw["q_row"], qw["s_row"], fw, Mx, Nx, Kx, c=c)
     for i in range(3):
         run(i)
-    med, avg = timed_events(run, rounds, torch.cuda.current_stream())
+    med, avg = timed_events(run, max(rounds // 5, 4), torch.cuda.current_stream())
     tf = 2.0 * Mx * Nx * Kx / (med * 1e-3) / 1e12
     del qa, qw, c
     torch.cuda.empty_cache()

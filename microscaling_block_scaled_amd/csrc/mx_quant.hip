@@ -14,12 +14,12 @@
 //                  max with two DPP quad exchanges.  Loads and stores of a wave
 //                  are contiguous.
 //   k_quant_tiles  column-wise layout stored transposed, optionally fused with
-//                  the row-wise one (one HBM read for both).  A 128 x 256 bf16
-//                  tile (128 x 128 fp32) is read with coalesced 16-byte loads,
-//                  row blocks are emitted from registers, the tile is staged
-//                  in LDS, and each lane then owns one 32-row column
-//                  block of a few columns; four consecutive lanes write 128
-//                  contiguous bytes of a transposed output row.
+//                  the row-wise one (one HBM read for both).  A 128 x 128 bf16
+//                  tile (128 x 64 fp32; 34 KB of LDS, so four workgroups fit
+//                  a CU) is read with coalesced 16-byte loads, row blocks are
+//                  emitted from registers, the tile is staged in LDS, and each
+//                  lane then owns the 32-row column blocks of one dword of
+//                  columns (two bf16 or one fp32).
 #include "mx_device.hpp"
 #include "mx_internal.h"
 
@@ -126,15 +126,37 @@ __device__ __forceinline__ Pack8 convert8(const uint32_t v[8], uint32_t code, co
 }
 
 // ---------------------------------------------------------------------------
+// streaming global accesses: every input byte is read once, and the row-wise
+// output is written in whole contiguous runs, so these bypass cache residency
+// (non-temporal).  The transposed output writes 24-32 byte pieces of many
+// rows; those stay ordinary stores so the L2 assembles whole lines.
+// ---------------------------------------------------------------------------
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_stream(const uint8_t* p) {
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream(uint8_t* p, uint4 v) {
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, (u32x4*)p);
+}
+__device__ __forceinline__ void st_stream(uint8_t* p, uint2 v) {
+  __builtin_nontemporal_store(u32x2{v.x, v.y}, (u32x2*)p);
+}
+__device__ __forceinline__ void st_stream(uint8_t* p, uint32_t v) {
+  __builtin_nontemporal_store(v, (uint32_t*)p);
+}
+
+// ---------------------------------------------------------------------------
 // stores
 // ---------------------------------------------------------------------------
 // 8 codes at element offset 8 * c of a packed row.
 template <int F>
 __device__ __forceinline__ void store8(uint8_t* row, int64_t c, const Pack8& o) {
   if (Fmt<F>::bits == 8) {
-    *(uint2*)(row + 8 * c) = make_uint2(o.w[0], o.w[1]);
+    st_stream(row + 8 * c, make_uint2(o.w[0], o.w[1]));
   } else if (Fmt<F>::bits == 4) {
-    *(uint32_t*)(row + 4 * c) = o.w[0];
+    st_stream(row + 4 * c, o.w[0]);
   } else {  // 6 bytes at 6c: dword + half, or half + dword, by parity
     uint8_t* p = row + 6 * c;
     if ((c & 1) == 0) {
@@ -147,7 +169,8 @@ __device__ __forceinline__ void store8(uint8_t* row, int64_t c, const Pack8& o) 
   }
 }
 
-// 32 codes (a whole block, four Pack8) at an aligned block position.
+// 32 codes (a whole block, four Pack8) at an aligned block position (ordinary
+// stores: see the streaming note above).
 template <int F>
 __device__ __forceinline__ void store32(uint8_t* p, const Pack8 o[4]) {
   if (Fmt<F>::bits == 8) {
@@ -253,7 +276,7 @@ struct QP {
   uint32_t signs;
   int lpr_log2;        // rows kernel: lanes per row (log2)
   int rows_per_block;  // rows kernel
-  int tiles_c;         // tile kernel: tiles along columns
+  int tiles_r, tiles_c;  // tile kernel: tiles along rows / columns
 };
 
 template <int SRC>
@@ -311,16 +334,17 @@ __device__ __forceinline__ void row_chunk(const QP& p, int64_t r, int64_t c, uin
 template <int SRC>
 __device__ __forceinline__ void load8(const uint8_t* rowp, int64_t c, uint32_t raw[8]) {
   if (SRC == SRC_BF16) {
-    const uint4 t = *(const uint4*)(rowp + 16 * c);
+    const uint4 t = ld_stream(rowp + 16 * c);
     raw[0] = t.x; raw[1] = t.y; raw[2] = t.z; raw[3] = t.w;
   } else {
-    const uint4 t0 = *(const uint4*)(rowp + 32 * c);
-    const uint4 t1 = *(const uint4*)(rowp + 32 * c + 16);
+    const uint4 t0 = ld_stream(rowp + 32 * c);
+    const uint4 t1 = ld_stream(rowp + 32 * c + 16);
     raw[0] = t0.x; raw[1] = t0.y; raw[2] = t0.z; raw[3] = t0.w;
     raw[4] = t1.x; raw[5] = t1.y; raw[6] = t1.z; raw[7] = t1.w;
   }
 }
 
+// 8-element chunks per lane in flight per row iteration
 constexpr int ROW_UNROLL = 4;
 
 template <int SRC, int F, bool SR, bool HAD>
@@ -357,13 +381,13 @@ __global__ __launch_bounds__(256) void k_quant_rows(QP p) {
 // ---------------------------------------------------------------------------
 template <int SRC> struct TileShape {
   static constexpr int ESZ = SRC == SRC_BF16 ? 2 : 4;  // source bytes per element
-  static constexpr int TC = SRC == SRC_BF16 ? 256 : 128;
-  static constexpr int TR = 128;
+  static constexpr int TC = 256 / ESZ;         // tile columns: 256 bytes of a source row
+  static constexpr int TR = 128;               // tile rows: four column blocks
   static constexpr int CPRW = TC / 8;          // 8-element chunks per tile row
   static constexpr int RPP = 256 / CPRW;       // tile rows per load pass
   static constexpr int PASSES = TR / RPP;
   static constexpr int RAWN = SRC == SRC_BF16 ? 4 : 8;  // dwords per chunk
-  static constexpr int CPT = SRC == SRC_BF16 ? 4 : 2;   // columns per lane, column pass
+  static constexpr int CPT = TC / 64;          // columns per lane, column pass
   static constexpr int PITCH = TC * ESZ + 16;  // LDS row pitch, padded
 };
 
@@ -417,11 +441,11 @@ __global__ __launch_bounds__(256) void k_quant_tiles(QP p) {
     if (row < tr_eff && col_ok) {
       const uint8_t* src = p.x + (r0 + row) * p.ld_bytes + c0 * T::ESZ;
       if (SRC == SRC_BF16) {
-        const uint4 t = *(const uint4*)(src + 16 * cq);
+        const uint4 t = ld_stream(src + 16 * cq);
         raw[pp][0] = t.x; raw[pp][1] = t.y; raw[pp][2] = t.z; raw[pp][3] = t.w;
       } else {
-        const uint4 t0 = *(const uint4*)(src + 32 * cq);
-        const uint4 t1 = *(const uint4*)(src + 32 * cq + 16);
+        const uint4 t0 = ld_stream(src + 32 * cq);
+        const uint4 t1 = ld_stream(src + 32 * cq + 16);
         raw[pp][0] = t0.x; raw[pp][1] = t0.y; raw[pp][2] = t0.z; raw[pp][3] = t0.w;
         raw[pp][4] = t1.x; raw[pp][5] = t1.y; raw[pp][6] = t1.z; raw[pp][7] = t1.w;
       }
@@ -450,18 +474,21 @@ __global__ __launch_bounds__(256) void k_quant_tiles(QP p) {
   }
   __syncthreads();
 
-  const int qb = tid & 3, g = tid >> 2;
+  // column pass: wave qb takes rows 32 qb .. 32 qb + 31 of the tile, lane g
+  // columns CPT g .. CPT g + CPT - 1; the lanes of a wave read one row's
+  // consecutive dwords (no bank conflicts)
+  const int qb = tid >> 6, g = tid & 63;
   if (32 * qb < tr_eff && g * T::CPT < tc_eff) {
-#pragma unroll 1
+    uint32_t w[32];
+#pragma unroll
+    for (int i = 0; i < 32; i++) w[i] = *(const uint32_t*)(lds + (32 * qb + i) * T::PITCH + g * 4);
+#pragma unroll
     for (int k = 0; k < T::CPT; k++) {
-      const int lc = g * T::CPT + k;
       uint32_t v[32];
 #pragma unroll
-      for (int i = 0; i < 32; i++) {
-        const uint8_t* s = lds + (32 * qb + i) * T::PITCH + lc * T::ESZ;
-        v[i] = SRC == SRC_BF16 ? ((uint32_t)(*(const uint16_t*)s) << 16) : *(const uint32_t*)s;
-      }
-      col_block<F, SR, HAD>(p, v, c0 + lc, r0 + 32 * qb);
+      for (int i = 0; i < 32; i++)
+        v[i] = SRC == SRC_BF16 ? (k == 0 ? w[i] << 16 : w[i] & 0xFFFF0000u) : w[i];
+      col_block<F, SR, HAD>(p, v, c0 + g * T::CPT + k, r0 + 32 * qb);
     }
   }
 }
@@ -508,12 +535,13 @@ static hipError_t tiles_launch(const QP& p0, bool rows, hipStream_t st) {
   QP p = p0;
   const int64_t tiles_r = (p.rows + T::TR - 1) / T::TR;
   const int64_t tiles_c = (p.cols + T::TC - 1) / T::TC;
+  p.tiles_r = (int)tiles_r;
   p.tiles_c = (int)tiles_c;
-  const dim3 grid((unsigned)(tiles_r * tiles_c));
+  const int64_t grid = tiles_r * tiles_c;
   if (rows)
-    hipLaunchKernelGGL((k_quant_tiles<SRC, F, SR, HAD, true>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_quant_tiles<SRC, F, SR, HAD, true>), dim3((unsigned)grid), dim3(256), 0, st, p);
   else
-    hipLaunchKernelGGL((k_quant_tiles<SRC, F, SR, HAD, false>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_quant_tiles<SRC, F, SR, HAD, false>), dim3((unsigned)grid), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
