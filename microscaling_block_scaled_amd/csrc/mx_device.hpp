@@ -139,6 +139,40 @@ __device__ __forceinline__ U4 sr_words(uint64_t seed, uint64_t counter_offset, u
 }
 
 // ---------------------------------------------------------------------------
+// buffer loads straight into LDS
+// ---------------------------------------------------------------------------
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over `bytes` bytes at `p` (gfx9 word 3: 32-bit data),
+// in scalar registers.
+__device__ __forceinline__ v4i make_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)p;
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Buffer load of `voff` (+ scalar `soff`) straight into LDS at `lds_dst`
+// (wave-uniform; lane i lands at lds_dst + 16 i).  One asm block that also
+// sets M0, so the compiler does not model it: every wait on it is explicit,
+// and LDS reads of the filled stage come after an asm barrier.  The
+// instruction has no register result.  A load that takes its LDS address
+// from M0 needs one wait state after the write of M0.
+__device__ __forceinline__ void dma16(v4i rs, uint32_t voff, uint32_t soff, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+               :
+               : "v"(voff), "s"(rs), "s"(lds_dst), "s"(soff)
+               : "memory", "m0");
+}
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// ---------------------------------------------------------------------------
 // DPP lane exchange inside groups of four lanes
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t quad_xor1(uint32_t v) {

@@ -15,11 +15,13 @@
 //                  are contiguous.
 //   k_quant_tiles  column-wise layout stored transposed, optionally fused with
 //                  the row-wise one (one HBM read for both).  A 128 x 128 bf16
-//                  tile (128 x 64 fp32; 34 KB of LDS, so four workgroups fit
-//                  a CU) is read with coalesced 16-byte loads, row blocks are
-//                  emitted from registers, the tile is staged in LDS, and each
-//                  lane then owns the 32-row column blocks of one dword of
-//                  columns (two bf16 or one fp32).
+//                  tile (128 x 64 fp32; 32 KB of LDS) is read with coalesced
+//                  16-byte loads, row blocks are emitted from registers with
+//                  whole-line streaming stores, the tile is staged in LDS, and
+//                  each lane then owns the 32-row column blocks of one dword of
+//                  columns (two bf16 or one fp32).  On whole tiles the four
+//                  blocks of a column sit in one lane quad, which writes the
+//                  column's transposed line in 64-byte runs.
 #include "mx_device.hpp"
 #include "mx_internal.h"
 
@@ -150,13 +152,17 @@ __device__ __forceinline__ void st_stream(uint8_t* p, uint32_t v) {
 // ---------------------------------------------------------------------------
 // stores
 // ---------------------------------------------------------------------------
-// 8 codes at element offset 8 * c of a packed row.
-template <int F>
+// 8 codes at element offset 8 * c of a packed row; non-temporal when NT (a
+// writer of whole lines), else ordinary stores that the L2 can merge with the
+// neighbouring pieces of the line.
+template <int F, bool NT = true>
 __device__ __forceinline__ void store8(uint8_t* row, int64_t c, const Pack8& o) {
   if (Fmt<F>::bits == 8) {
-    st_stream(row + 8 * c, make_uint2(o.w[0], o.w[1]));
+    if (NT) st_stream(row + 8 * c, make_uint2(o.w[0], o.w[1]));
+    else *(uint2*)(row + 8 * c) = make_uint2(o.w[0], o.w[1]);
   } else if (Fmt<F>::bits == 4) {
-    st_stream(row + 4 * c, o.w[0]);
+    if (NT) st_stream(row + 4 * c, o.w[0]);
+    else *(uint32_t*)(row + 4 * c) = o.w[0];
   } else {  // 6 bytes at 6c: dword + half, or half + dword, by parity
     uint8_t* p = row + 6 * c;
     if ((c & 1) == 0) {
@@ -300,7 +306,7 @@ __device__ __forceinline__ void widen8(const uint32_t* raw, uint32_t v[8]) {
 // flushed before the transform; after it no flush is needed: a subnormal
 // block maximum gives scale code 0 either way, and the conversions treat a
 // subnormal element as zero.
-template <int F, bool SR, bool HAD>
+template <int F, bool SR, bool HAD, bool NT = true>
 __device__ __forceinline__ void row_chunk(const QP& p, int64_t r, int64_t c, uint32_t v[8],
                                           const HadLane& hl) {
   const int q = (int)(c & 3);
@@ -325,7 +331,7 @@ __device__ __forceinline__ void row_chunk(const QP& p, int64_t r, int64_t c, uin
     rnd[4] = b.x; rnd[5] = b.y; rnd[6] = b.z; rnd[7] = b.w;
   }
   const Pack8 o = convert8<F, SR>(v, code, rnd);
-  store8<F>(p.q_row + r * p.qr_pitch, c, o);
+  store8<F, NT>(p.q_row + r * p.qr_pitch, c, o);
 }
 
 // ---------------------------------------------------------------------------
@@ -383,16 +389,19 @@ template <int SRC> struct TileShape {
   static constexpr int ESZ = SRC == SRC_BF16 ? 2 : 4;  // source bytes per element
   static constexpr int TC = 256 / ESZ;         // tile columns: 256 bytes of a source row
   static constexpr int TR = 128;               // tile rows: four column blocks
+  static constexpr int ROWB = 256;             // LDS bytes per tile row
   static constexpr int CPRW = TC / 8;          // 8-element chunks per tile row
   static constexpr int RPP = 256 / CPRW;       // tile rows per load pass
   static constexpr int PASSES = TR / RPP;
   static constexpr int RAWN = SRC == SRC_BF16 ? 4 : 8;  // dwords per chunk
   static constexpr int CPT = TC / 64;          // columns per lane, column pass
-  static constexpr int PITCH = TC * ESZ + 16;  // LDS row pitch, padded
 };
 
+// Scale code and packed codes of the column block at column `col`, rows
+// rs .. rs + 31 (v: its 32 elements as fp32 bits).
 template <int F, bool SR, bool HAD>
-__device__ __forceinline__ void col_block(const QP& p, uint32_t v[32], int64_t col, int64_t rs) {
+__device__ __forceinline__ uint32_t col_codes(const QP& p, uint32_t v[32], int64_t col, int64_t rs,
+                                              Pack8 o[4]) {
   if (HAD) {
 #pragma unroll
     for (int k = 0; k < 32; k++) v[k] = daz32(v[k]);
@@ -402,8 +411,6 @@ __device__ __forceinline__ void col_block(const QP& p, uint32_t v[32], int64_t c
 #pragma unroll
   for (int k = 0; k < 32; k++) am = umax(am, v[k] & 0x7FFFFFFFu);
   const uint32_t code = scale_code<F>(am);
-  p.s_colt[col * (p.rows >> 5) + (rs >> 5)] = (uint8_t)code;
-  Pack8 o[4];
 #pragma unroll
   for (int h = 0; h < 4; h++) {
     uint32_t rnd[8];
@@ -418,18 +425,77 @@ __device__ __forceinline__ void col_block(const QP& p, uint32_t v[32], int64_t c
     }
     o[h] = convert8<F, SR>(&v[8 * h], code, rnd);
   }
+  return code;
+}
+
+template <int F, bool SR, bool HAD>
+__device__ __forceinline__ void col_block(const QP& p, uint32_t v[32], int64_t col, int64_t rs) {
+  Pack8 o[4];
+  const uint32_t code = col_codes<F, SR, HAD>(p, v, col, rs, o);
+  p.s_colt[col * (p.rows >> 5) + (rs >> 5)] = (uint8_t)code;
   store32<F>(p.q_colt + col * p.qc_pitch + (rs * Fmt<F>::bits) / 8, o);
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t quad_perm(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Column block qb (rows r0 + 32 qb ..) of column `col`, held by lane qb of a
+// quad whose four lanes hold the column's four blocks of the tile.  With
+// 8-bit codes the quad's 128 transposed bytes are exchanged so that each store
+// instruction writes 64 contiguous bytes per quad: lane q first writes bytes
+// 16 q .. 16 q + 15 (half q & 1 of block q >> 1), then 64 + 16 q .. (half
+// q & 1 of block 2 + (q >> 1)).
+template <int F, bool SR, bool HAD>
+__device__ __forceinline__ void col_quad(const QP& p, uint32_t v[32], int64_t col, int64_t r0, int qb) {
+  Pack8 o[4];
+  const int64_t rs = r0 + 32 * qb;
+  const uint32_t code = col_codes<F, SR, HAD>(p, v, col, rs, o);
+  p.s_colt[col * (p.rows >> 5) + (rs >> 5)] = (uint8_t)code;
+  if (Fmt<F>::bits == 8) {
+    const uint32_t d[8] = {o[0].w[0], o[0].w[1], o[1].w[0], o[1].w[1],
+                           o[2].w[0], o[2].w[1], o[3].w[0], o[3].w[1]};
+    const bool odd = qb & 1;
+    uint32_t e[8];
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+      // Both halves are moved on every lane before the per-lane choice: the
+      // empty asm pins the exchanges to uniform control flow, so the compiler
+      // cannot turn the choice into branches that leave source lanes inactive.
+      uint32_t a0 = quad_perm<0x50>(d[m]), a1 = quad_perm<0x50>(d[4 + m]);  // from lanes [0,0,1,1]
+      uint32_t b0 = quad_perm<0xFA>(d[m]), b1 = quad_perm<0xFA>(d[4 + m]);  // from lanes [2,2,3,3]
+      asm volatile("" : "+v"(a0), "+v"(a1), "+v"(b0), "+v"(b1));
+      e[m] = odd ? a1 : a0;
+      e[4 + m] = odd ? b1 : b0;
+    }
+    uint8_t* line = p.q_colt + col * p.qc_pitch + r0;
+    *(uint4*)(line + 16 * qb) = make_uint4(e[0], e[1], e[2], e[3]);
+    *(uint4*)(line + 64 + 16 * qb) = make_uint4(e[4], e[5], e[6], e[7]);
+  } else {
+    store32<F>(p.q_colt + col * p.qc_pitch + (rs * Fmt<F>::bits) / 8, o);
+  }
+}
+
+// 16-byte piece p of tile row r sits at piece p ^ tile_swz(r) of its LDS row
+// in a whole tile: the column pass reads rows 32 apart together, and rows 32
+// apart fall in different banks.
+__device__ __forceinline__ int tile_swz(int r) { return ((r >> 5) & 3) * 4; }
+
+// Whole tiles: the column pass gives lane 4 c + qb of wave w the dword
+// 16 w + c of rows 32 qb .. 32 qb + 31, so a quad holds the four blocks of its
+// columns (one 128-byte transposed line each for 8-bit codes).  Ragged edge
+// tiles: wave qb takes rows 32 qb .., lane g the dword g.
 template <int SRC, int F, bool SR, bool HAD, bool ROWS>
 __global__ __launch_bounds__(256) void k_quant_tiles(QP p) {
   using T = TileShape<SRC>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[T::TR * T::PITCH];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[T::TR * T::ROWB];
   const int tid = threadIdx.x;
   const int64_t tr = blockIdx.x / p.tiles_c, tc = blockIdx.x % p.tiles_c;
   const int64_t r0 = tr * T::TR, c0 = tc * T::TC;
   const int tr_eff = (int)(p.rows - r0 < T::TR ? p.rows - r0 : T::TR);
   const int tc_eff = (int)(p.cols - c0 < T::TC ? p.cols - c0 : T::TC);
+  const bool whole = tr_eff == T::TR && tc_eff == T::TC;
   const int cq = tid % T::CPRW, sub = tid / T::CPRW;
   const HadLane hl = had_lane(p.signs, cq & 3);  // tile columns start at a multiple of 4 chunks
   const bool col_ok = cq * 8 < tc_eff;
@@ -463,32 +529,47 @@ __global__ __launch_bounds__(256) void k_quant_tiles(QP p) {
         for (int k = 0; k < 8; k++) w[k] = v[k];
         row_chunk<F, SR, HAD>(p, r0 + row, (c0 >> 3) + cq, w, hl);
       }
-      uint8_t* dst = lds + row * T::PITCH + cq * 8 * T::ESZ;
+      const int sw = whole ? tile_swz(row) : 0;
+      uint8_t* dst = lds + row * T::ROWB;
       if (SRC == SRC_BF16) {
-        *(uint4*)dst = make_uint4(raw[pp][0], raw[pp][1], raw[pp][2], raw[pp][3]);
+        *(uint4*)(dst + 16 * (cq ^ sw)) = make_uint4(raw[pp][0], raw[pp][1], raw[pp][2], raw[pp][3]);
       } else {
-        *(uint4*)dst = make_uint4(v[0], v[1], v[2], v[3]);
-        *(uint4*)(dst + 16) = make_uint4(v[4], v[5], v[6], v[7]);
+        *(uint4*)(dst + 16 * ((2 * cq) ^ sw)) = make_uint4(v[0], v[1], v[2], v[3]);
+        *(uint4*)(dst + 16 * ((2 * cq + 1) ^ sw)) = make_uint4(v[4], v[5], v[6], v[7]);
       }
     }
   }
   __syncthreads();
 
-  // column pass: wave qb takes rows 32 qb .. 32 qb + 31 of the tile, lane g
-  // columns CPT g .. CPT g + CPT - 1; the lanes of a wave read one row's
-  // consecutive dwords (no bank conflicts)
-  const int qb = tid >> 6, g = tid & 63;
-  if (32 * qb < tr_eff && g * T::CPT < tc_eff) {
+  if (whole) {
+    const int lane = tid & 63, qb = lane & 3;
+    const int d = 16 * (tid >> 6) + (lane >> 2);
+    const uint8_t* src = lds + 32 * qb * T::ROWB + 16 * ((d >> 2) ^ (4 * qb)) + 4 * (d & 3);
     uint32_t w[32];
 #pragma unroll
-    for (int i = 0; i < 32; i++) w[i] = *(const uint32_t*)(lds + (32 * qb + i) * T::PITCH + g * 4);
+    for (int i = 0; i < 32; i++) w[i] = *(const uint32_t*)(src + i * T::ROWB);
 #pragma unroll
     for (int k = 0; k < T::CPT; k++) {
       uint32_t v[32];
 #pragma unroll
       for (int i = 0; i < 32; i++)
         v[i] = SRC == SRC_BF16 ? (k == 0 ? w[i] << 16 : w[i] & 0xFFFF0000u) : w[i];
-      col_block<F, SR, HAD>(p, v, c0 + g * T::CPT + k, r0 + 32 * qb);
+      col_quad<F, SR, HAD>(p, v, c0 + T::CPT * d + k, r0, qb);
+    }
+  } else {
+    const int qb = tid >> 6, g = tid & 63;
+    if (32 * qb < tr_eff && g * T::CPT < tc_eff) {
+      uint32_t w[32];
+#pragma unroll
+      for (int i = 0; i < 32; i++) w[i] = *(const uint32_t*)(lds + (32 * qb + i) * T::ROWB + g * 4);
+#pragma unroll
+      for (int k = 0; k < T::CPT; k++) {
+        uint32_t v[32];
+#pragma unroll
+        for (int i = 0; i < 32; i++)
+          v[i] = SRC == SRC_BF16 ? (k == 0 ? w[i] << 16 : w[i] & 0xFFFF0000u) : w[i];
+        col_block<F, SR, HAD>(p, v, c0 + g * T::CPT + k, r0 + 32 * qb);
+      }
     }
   }
 }

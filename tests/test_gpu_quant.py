@@ -100,6 +100,22 @@ def test_dual_layout_e4m3(mx, oracle):
     assert torch.equal(both["q_colt"], col["q_colt"]) and torch.equal(both["s_colt"], col["s_colt"])
 
 
+@pytest.mark.parametrize("fmt", range(6))
+def test_whole_tile_shapes(mx, oracle, fmt):
+    """Shapes made of whole tiles (128 rows x 256 source bytes), which take the
+    tile kernel's whole-tile column pass, in bf16 and fp32."""
+    from microscaling_block_scaled_amd.synth import make
+    x = make("dual_quant", {"X": (2560, 3840)}, seed=6)["X"]
+    for lay in (2, 3):
+        run_both(mx, oracle, x, fmt, lay, 0, what=f"whole tiles lay{lay}")
+    run_both(mx, oracle, x, fmt, 3, 1, True, 0x1234567, 9, 0, what="whole tiles dual h32 sr")
+    rng = np.random.default_rng(fmt)
+    x32 = (rng.standard_t(3, (3072, 1600)) * np.exp2(rng.uniform(-30, 30, (3072, 1)))).astype(np.float32)
+    x32[5, :64] = np.float32(1e-40)
+    run_both(mx, oracle, x32, fmt, 3, 0, what="whole fp32 tiles dual")
+    run_both(mx, oracle, x32, fmt, 2, 1, seed=4, off=2, what="whole fp32 tiles col sr")
+
+
 @pytest.mark.parametrize("fmt", [4, 0, 2])
 def test_hadamard_and_sr(mx, oracle, fmt):
     """The FP4 recipe: Hadamard-32 on every block, SR (seed 42) on A, RNE on W;
