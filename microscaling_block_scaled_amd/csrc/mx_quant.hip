@@ -89,6 +89,59 @@ __device__ __forceinline__ Pack8 hw_convert8(const uint32_t v[8], uint32_t code)
   return o;
 }
 
+// The same conversion of 8 bf16 elements held packed in raw[4] (element 2i in
+// the low half of raw[i]), through the packed-bf16 form of the instructions;
+// bf16 widens to fp32 exactly, so the codes are the same.
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+template <int F>
+__device__ __forceinline__ Pack8 hw_convert8_bf16(const uint32_t raw[4], uint32_t code) {
+  const float S = __builtin_bit_cast(float, code << 23);
+  Pack8 o;
+  if (F == E4M3 || F == E5M2) {
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const v2bf a = __builtin_bit_cast(v2bf, raw[2 * h]), b = __builtin_bit_cast(v2bf, raw[2 * h + 1]);
+      v2s t = {0, 0};
+      if (F == E4M3) {
+        t = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(t, a, S, false);
+        t = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(t, b, S, true);
+      } else {
+        t = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(t, a, S, false);
+        t = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(t, b, S, true);
+      }
+      o.w[h] = fix_sat<F>(__builtin_bit_cast(uint32_t, t));
+    }
+  } else {  // E2M1
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf, raw[0]), S, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf, raw[1]), S, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf, raw[2]), S, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf, raw[3]), S, 3);
+    o.w[0] = r;
+    o.w[1] = 0;
+  }
+  return o;
+}
+
+// Formats with a hardware conversion that matches the definition (round to
+// nearest even only).
+template <int F, bool SR> struct HwPath {
+  static constexpr bool value = !SR && (F == E4M3 || F == E5M2 || F == E2M1);
+};
+// Whether a block with scale `code` can take the hardware conversion.
+template <int F>
+__device__ __forceinline__ bool hw_ok(uint32_t code) {
+  return code >= (uint32_t)DazFree<F>::value && code != 0xFFu;
+}
+
+// Largest magnitude of the bf16 pairs in w[0 .. n-1], per half: packed 16-bit
+// unsigned max of the sign-cleared pairs (a magnitude compare for bf16).
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+
 template <int F>
 __device__ __forceinline__ Pack8 pack8(const uint32_t c[8]) {
   Pack8 o;
@@ -334,6 +387,40 @@ __device__ __forceinline__ void row_chunk(const QP& p, int64_t r, int64_t c, uin
   store8<F, NT>(p.q_row + r * p.qr_pitch, c, o);
 }
 
+// row_chunk for 8 bf16 elements held packed in raw[4], without stochastic
+// rounding or the transform, for formats with a hardware conversion: the
+// block max and the conversion work on the packed pairs.
+//  `sc`: where the block's scale byte goes instead of s_row when not null (a
+// staging buffer in LDS).
+template <int F, bool NT = true>
+__device__ __forceinline__ void row_chunk_bf16(const QP& p, int64_t r, int64_t c, const uint32_t raw[4],
+                                               uint8_t* sc = nullptr) {
+  const int q = (int)(c & 3);
+  const uint32_t m = pk_max_u16(pk_max_u16(raw[0] & 0x7FFF7FFFu, raw[1] & 0x7FFF7FFFu),
+                                pk_max_u16(raw[2] & 0x7FFF7FFFu, raw[3] & 0x7FFF7FFFu));
+  uint32_t am = umax(m << 16, m & 0xFFFF0000u);  // as fp32 bits
+  am = umax(am, quad_xor1(am));
+  am = umax(am, quad_xor2(am));
+  const uint32_t code = scale_code<F>(am);
+  if (q == 0) {
+    if (sc) *sc = (uint8_t)code;
+    else p.s_row[r * (p.cols >> 5) + (c >> 2)] = (uint8_t)code;
+  }
+  Pack8 o;
+  if (hw_ok<F>(code)) {
+    o = hw_convert8_bf16<F>(raw, code);
+  } else {
+    uint32_t v[8], rnd[8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      v[2 * i] = raw[i] << 16;
+      v[2 * i + 1] = raw[i] & 0xFFFF0000u;
+    }
+    o = convert8<F, false>(v, code, rnd);
+  }
+  store8<F, NT>(p.q_row + r * p.qr_pitch, c, o);
+}
+
 // ---------------------------------------------------------------------------
 // row-wise kernel
 // ---------------------------------------------------------------------------
@@ -373,9 +460,13 @@ __global__ __launch_bounds__(256) void k_quant_rows(QP p) {
 #pragma unroll
       for (int u = 0; u < ROW_UNROLL; u++) {
         if (c + u * lpr < cpr) {
-          uint32_t v[8];
-          widen8<SRC>(raw[u], v);
-          row_chunk<F, SR, HAD>(p, r, c + u * lpr, v, hl);
+          if constexpr (SRC == SRC_BF16 && !HAD && HwPath<F, SR>::value) {
+            row_chunk_bf16<F>(p, r, c + u * lpr, raw[u]);
+          } else {
+            uint32_t v[8];
+            widen8<SRC>(raw[u], v);
+            row_chunk<F, SR, HAD>(p, r, c + u * lpr, v, hl);
+          }
         }
       }
     }
@@ -447,12 +538,11 @@ __device__ __forceinline__ uint32_t quad_perm(uint32_t v) {
 // instruction writes 64 contiguous bytes per quad: lane q first writes bytes
 // 16 q .. 16 q + 15 (half q & 1 of block q >> 1), then 64 + 16 q .. (half
 // q & 1 of block 2 + (q >> 1)).
-template <int F, bool SR, bool HAD>
-__device__ __forceinline__ void col_quad(const QP& p, uint32_t v[32], int64_t col, int64_t r0, int qb) {
-  Pack8 o[4];
+template <int F, bool SCALE = true>
+__device__ __forceinline__ void col_quad_store(const QP& p, const Pack8 o[4], uint32_t code, int64_t col,
+                                               int64_t r0, int qb) {
   const int64_t rs = r0 + 32 * qb;
-  const uint32_t code = col_codes<F, SR, HAD>(p, v, col, rs, o);
-  p.s_colt[col * (p.rows >> 5) + (rs >> 5)] = (uint8_t)code;
+  if (SCALE) p.s_colt[col * (p.rows >> 5) + (rs >> 5)] = (uint8_t)code;
   if (Fmt<F>::bits == 8) {
     const uint32_t d[8] = {o[0].w[0], o[0].w[1], o[1].w[0], o[1].w[1],
                            o[2].w[0], o[2].w[1], o[3].w[0], o[3].w[1]};
@@ -477,6 +567,67 @@ __device__ __forceinline__ void col_quad(const QP& p, uint32_t v[32], int64_t co
   }
 }
 
+template <int F, bool SR, bool HAD>
+__device__ __forceinline__ void col_quad(const QP& p, uint32_t v[32], int64_t col, int64_t r0, int qb) {
+  Pack8 o[4];
+  const uint32_t code = col_codes<F, SR, HAD>(p, v, col, r0 + 32 * qb, o);
+  col_quad_store<F>(p, o, code, col, r0, qb);
+}
+
+// Whole-tile column pass on bf16 pairs without stochastic rounding or the
+// transform, for formats with a hardware conversion: w[i] holds columns col
+// (low half) and col + 1 (high half) of row 32 qb + i.  Both block maxima come
+// from one packed max; each column's pairs of rows are regrouped with a byte
+// permute for the packed conversion.
+template <int F>
+__device__ __forceinline__ void col_pair_bf16(const QP& p, const uint32_t w[32], int64_t col, int64_t r0,
+                                              int qb) {
+  const bool gather = (p.rows & 127) == 0;  // a quad's scale bytes make an aligned dword
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 32; i++) m = pk_max_u16(m, w[i] & 0x7FFF7FFFu);
+  const uint32_t codes[2] = {scale_code<F>(m << 16), scale_code<F>(m & 0xFFFF0000u)};
+  // The quad's four scale bytes of each column are one dword of s_colt: lane
+  // 0 of the quad writes the first column's, lane 1 the second's.
+  uint32_t g[2];
+#pragma unroll
+  for (int k = 0; k < 2; k++) {
+    uint32_t a = quad_perm<0xB1>(codes[k]);  // from lanes [1,0,3,2]
+    asm volatile("" : "+v"(a));
+    a = codes[k] | (a << 8);
+    uint32_t b = quad_perm<0x4E>(a);  // from lanes [2,3,0,1]
+    asm volatile("" : "+v"(b));
+    g[k] = a | (b << 16);  // complete on lane 0
+  }
+  uint32_t g1 = quad_perm<0x00>(g[1]);  // lane 0's to every lane
+  asm volatile("" : "+v"(g1));
+  if (gather && qb < 2)
+    *(uint32_t*)(p.s_colt + (col + qb) * (p.rows >> 5) + (r0 >> 5)) = qb == 0 ? g[0] : g1;
+#pragma unroll
+  for (int k = 0; k < 2; k++) {
+    const uint32_t code = codes[k];
+    Pack8 o[4];
+    if (hw_ok<F>(code)) {
+#pragma unroll
+      for (int h = 0; h < 4; h++) {
+        uint32_t pr[4];  // rows 8 h + 2 j, 8 h + 2 j + 1 of this column
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          pr[j] = __builtin_amdgcn_perm(w[8 * h + 2 * j + 1], w[8 * h + 2 * j], k == 0 ? 0x05040100u : 0x07060302u);
+        o[h] = hw_convert8_bf16<F>(pr, code);
+      }
+    } else {
+      uint32_t v[32], rnd[8];
+#pragma unroll
+      for (int i = 0; i < 32; i++) v[i] = k == 0 ? w[i] << 16 : w[i] & 0xFFFF0000u;
+#pragma unroll
+      for (int h = 0; h < 4; h++) o[h] = convert8<F, false>(&v[8 * h], code, rnd);
+    }
+    if (!gather) p.s_colt[(col + k) * (p.rows >> 5) + (r0 >> 5) + qb] = (uint8_t)code;
+    col_quad_store<F, false>(p, o, code, col + k, r0, qb);
+  }
+}
+
 // 16-byte piece p of tile row r sits at piece p ^ tile_swz(r) of its LDS row
 // in a whole tile: the column pass reads rows 32 apart together, and rows 32
 // apart fall in different banks.
@@ -490,12 +641,17 @@ template <int SRC, int F, bool SR, bool HAD, bool ROWS>
 __global__ __launch_bounds__(256) void k_quant_tiles(QP p) {
   using T = TileShape<SRC>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[T::TR * T::ROWB];
+  __shared__ uint32_t sc_lds[T::TR];  // row-wise scale bytes of a whole tile, one dword per row
   const int tid = threadIdx.x;
   const int64_t tr = blockIdx.x / p.tiles_c, tc = blockIdx.x % p.tiles_c;
   const int64_t r0 = tr * T::TR, c0 = tc * T::TC;
   const int tr_eff = (int)(p.rows - r0 < T::TR ? p.rows - r0 : T::TR);
   const int tc_eff = (int)(p.cols - c0 < T::TC ? p.cols - c0 : T::TC);
   const bool whole = tr_eff == T::TR && tc_eff == T::TC;
+  // whole bf16 tiles with rows of s_row in whole dwords: the row-wise scales
+  // are gathered in LDS and written one dword per row
+  constexpr bool FAST = SRC == SRC_BF16 && !HAD && HwPath<F, SR>::value;
+  const bool gather = FAST && ROWS && whole && (p.cols & 127) == 0;
   const int cq = tid % T::CPRW, sub = tid / T::CPRW;
   const HadLane hl = had_lane(p.signs, cq & 3);  // tile columns start at a multiple of 4 chunks
   const bool col_ok = cq * 8 < tc_eff;
@@ -506,7 +662,7 @@ __global__ __launch_bounds__(256) void k_quant_tiles(QP p) {
     const int row = pp * T::RPP + sub;
     if (row < tr_eff && col_ok) {
       const uint8_t* src = p.x + (r0 + row) * p.ld_bytes + c0 * T::ESZ;
-      if (SRC == SRC_BF16) {
+      if constexpr (SRC == SRC_BF16) {
         const uint4 t = ld_stream(src + 16 * cq);
         raw[pp][0] = t.x; raw[pp][1] = t.y; raw[pp][2] = t.z; raw[pp][3] = t.w;
       } else {
@@ -517,6 +673,10 @@ __global__ __launch_bounds__(256) void k_quant_tiles(QP p) {
       }
     }
   }
+  // All of the tile is needed before the first stores go out.  Waiting for
+  // the loads here, explicitly, tells the compiler they are complete, so it
+  // does not wait again (for the stores then in flight) before each pass.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 #pragma unroll
   for (int pp = 0; pp < T::PASSES; pp++) {
     const int row = pp * T::RPP + sub;
@@ -524,14 +684,19 @@ __global__ __launch_bounds__(256) void k_quant_tiles(QP p) {
       uint32_t v[8];
       widen8<SRC>(raw[pp], v);
       if (ROWS) {
-        uint32_t w[8];
+        if constexpr (FAST) {
+          row_chunk_bf16<F>(p, r0 + row, (c0 >> 3) + cq, raw[pp],
+                            gather ? (uint8_t*)sc_lds + 4 * row + (cq >> 2) : nullptr);
+        } else {
+          uint32_t w[8];
 #pragma unroll
-        for (int k = 0; k < 8; k++) w[k] = v[k];
-        row_chunk<F, SR, HAD>(p, r0 + row, (c0 >> 3) + cq, w, hl);
+          for (int k = 0; k < 8; k++) w[k] = v[k];
+          row_chunk<F, SR, HAD>(p, r0 + row, (c0 >> 3) + cq, w, hl);
+        }
       }
       const int sw = whole ? tile_swz(row) : 0;
       uint8_t* dst = lds + row * T::ROWB;
-      if (SRC == SRC_BF16) {
+      if constexpr (SRC == SRC_BF16) {
         *(uint4*)(dst + 16 * (cq ^ sw)) = make_uint4(raw[pp][0], raw[pp][1], raw[pp][2], raw[pp][3]);
       } else {
         *(uint4*)(dst + 16 * ((2 * cq) ^ sw)) = make_uint4(v[0], v[1], v[2], v[3]);
@@ -541,6 +706,8 @@ __global__ __launch_bounds__(256) void k_quant_tiles(QP p) {
   }
   __syncthreads();
 
+  if (gather && tid < T::TR)
+    *(uint32_t*)(p.s_row + (r0 + tid) * (p.cols >> 5) + (c0 >> 5)) = sc_lds[tid];
   if (whole) {
     const int lane = tid & 63, qb = lane & 3;
     const int d = 16 * (tid >> 6) + (lane >> 2);
@@ -548,13 +715,17 @@ __global__ __launch_bounds__(256) void k_quant_tiles(QP p) {
     uint32_t w[32];
 #pragma unroll
     for (int i = 0; i < 32; i++) w[i] = *(const uint32_t*)(src + i * T::ROWB);
+    if constexpr (FAST) {
+      col_pair_bf16<F>(p, w, c0 + 2 * d, r0, qb);
+    } else {
 #pragma unroll
-    for (int k = 0; k < T::CPT; k++) {
-      uint32_t v[32];
+      for (int k = 0; k < T::CPT; k++) {
+        uint32_t v[32];
 #pragma unroll
-      for (int i = 0; i < 32; i++)
-        v[i] = SRC == SRC_BF16 ? (k == 0 ? w[i] << 16 : w[i] & 0xFFFF0000u) : w[i];
-      col_quad<F, SR, HAD>(p, v, c0 + T::CPT * d + k, r0, qb);
+        for (int i = 0; i < 32; i++)
+          v[i] = SRC == SRC_BF16 ? (k == 0 ? w[i] << 16 : w[i] & 0xFFFF0000u) : w[i];
+        col_quad<F, SR, HAD>(p, v, c0 + T::CPT * d + k, r0, qb);
+      }
     }
   } else {
     const int qb = tid >> 6, g = tid & 63;
