@@ -264,6 +264,13 @@ def main():
         ks["gemm_mxfp8_grad"] = bench_gemm(mx, "E5M2 x E4M3 M=4096 N=4096 K=14336", d["A"],
                                            d["W"], mx.E5M2, mx.E4M3, PEAK_TFLOPS["fp8"])
         del d
+        # the 6-bit and mixed 4/6-bit variants of the MXFP4 MLP product
+        d = make("mxfp4_mlp")
+        ks["gemm_mxfp6_mlp"] = bench_gemm(mx, "E2M3 x E2M3 M=8192 N=4096 K=14336", d["A"], d["W"],
+                                          mx.E2M3, mx.E2M3, PEAK_TFLOPS["fp6"])
+        ks["gemm_mxfp6x4_mlp"] = bench_gemm(mx, "E2M3 activations x E2M1 weights M=8192 N=4096 K=14336",
+                                            d["A"], d["W"], mx.E2M3, mx.E2M1, PEAK_TFLOPS["fp6"])
+        del d
         out["kernels"] = ks
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()

@@ -336,6 +336,7 @@ struct QP {
   int lpr_log2;        // rows kernel: lanes per row (log2)
   int rows_per_block;  // rows kernel
   int tiles_r, tiles_c;  // tile kernel: tiles along rows / columns
+  int wpr;               // block kernel: waves per row (64 blocks each)
 };
 
 template <int SRC>
@@ -471,6 +472,81 @@ __global__ __launch_bounds__(256) void k_quant_rows(QP p) {
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// block kernel: row-wise layout with one whole block per lane
+// ---------------------------------------------------------------------------
+// Used with the Hadamard transform: all five butterfly stages then run in a
+// lane's registers (no lane exchanges), and the block max needs no reduction
+// across lanes.  Wave g of the grid takes 64 consecutive blocks of row
+// g / wpr; a lane reads its block's 64 (bf16) or 128 (fp32) bytes and writes
+// its packed codes as one run.
+template <int F>
+__device__ __forceinline__ void store32_stream(uint8_t* p, const Pack8 o[4]) {
+  if (Fmt<F>::bits == 8) {
+    st_stream(p, make_uint4(o[0].w[0], o[0].w[1], o[1].w[0], o[1].w[1]));
+    st_stream(p + 16, make_uint4(o[2].w[0], o[2].w[1], o[3].w[0], o[3].w[1]));
+  } else if (Fmt<F>::bits == 4) {
+    st_stream(p, make_uint4(o[0].w[0], o[1].w[0], o[2].w[0], o[3].w[0]));
+  } else {
+    store32<F>(p, o);
+  }
+}
+
+template <int SRC, int F, bool SR, bool HAD>
+__global__ __launch_bounds__(256) void k_quant_blocks(QP p) {
+  constexpr int ESZ = SRC == SRC_BF16 ? 2 : 4;
+  const int lane = threadIdx.x & 63;
+  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t r = g / p.wpr;
+  const int64_t kb = (g % p.wpr) * 64 + lane;  // block of row r
+  const int64_t bpr = p.cols >> 5;
+  if (r >= p.rows || kb >= bpr) return;  // no lane exchanges below
+  const uint8_t* src = p.x + r * p.ld_bytes + kb * 32 * ESZ;
+  uint32_t v[32];
+  if (SRC == SRC_BF16) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const uint4 t = *(const uint4*)(src + 16 * j);
+      const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        v[8 * j + 2 * i] = w[i] << 16;
+        v[8 * j + 2 * i + 1] = w[i] & 0xFFFF0000u;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const uint4 t = *(const uint4*)(src + 16 * j);
+      v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
+    }
+  }
+  if (HAD) {
+#pragma unroll
+    for (int k = 0; k < 32; k++) v[k] = daz32(v[k]);
+    hadamard_local(v, p.signs);
+  }
+  uint32_t am = 0;
+#pragma unroll
+  for (int k = 0; k < 32; k++) am = umax(am, v[k] & 0x7FFFFFFFu);
+  const uint32_t code = scale_code<F>(am);
+  p.s_row[r * bpr + kb] = (uint8_t)code;
+  Pack8 o[4];
+#pragma unroll
+  for (int h = 0; h < 4; h++) {
+    uint32_t rnd[8];
+    if (SR) {
+      const uint64_t c = (uint64_t)(r * p.cols + kb * 32 + 8 * h) >> 2;
+      const U4 a = sr_words(p.seed, p.off, 0u, c);
+      const U4 b = sr_words(p.seed, p.off, 0u, c + 1);
+      rnd[0] = a.x; rnd[1] = a.y; rnd[2] = a.z; rnd[3] = a.w;
+      rnd[4] = b.x; rnd[5] = b.y; rnd[6] = b.z; rnd[7] = b.w;
+    }
+    o[h] = convert8<F, SR>(&v[8 * h], code, rnd);
+  }
+  store32_stream<F>(p.q_row + r * p.qr_pitch + kb * 4 * Fmt<F>::bits, o);
 }
 
 // ---------------------------------------------------------------------------
@@ -770,6 +846,13 @@ static QP make_qp(const QuantArgs& a) {
 template <int SRC, int F, bool SR, bool HAD>
 static hipError_t rows_launch(const QP& p0, hipStream_t st) {
   QP p = p0;
+  if constexpr (HAD) {
+    const int64_t wpr = (p.cols / 32 + 63) / 64;
+    p.wpr = (int)wpr;
+    const int64_t waves = p.rows * wpr;
+    hipLaunchKernelGGL((k_quant_blocks<SRC, F, SR, HAD>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, p);
+    return hipGetLastError();
+  }
   const int64_t cpr = p.cols / 8;
   int lg = 6;  // up to a wave per row
   while (lg > 2 && ((int64_t)1 << lg) > cpr) lg--;
