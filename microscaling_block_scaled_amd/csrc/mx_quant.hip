@@ -9,10 +9,9 @@
 // block before scaling.
 //
 // Two kernels:
-//   k_quant_rows   row-wise layout.  A lane owns 8 consecutive elements (one
-//                  16-byte bf16 load); four lanes hold one block and reduce its
-//                  max with two DPP quad exchanges.  Loads and stores of a wave
-//                  are contiguous.
+//   k_quant_blocks row-wise layout.  A lane owns one whole 32-element block:
+//                  the transform's butterflies and the block max stay in its
+//                  registers, and its packed codes go out as one run.
 //   k_quant_tiles  column-wise layout stored transposed, optionally fused with
 //                  the row-wise one (one HBM read for both).  A 128 x 128 bf16
 //                  tile (128 x 64 fp32; 32 KB of LDS) is read with coalesced
@@ -161,6 +160,27 @@ __device__ __forceinline__ Pack8 pack8(const uint32_t c[8]) {
   return o;
 }
 
+// INT8 codes of 8 elements (fp32 bits) with scale `code`, round to nearest
+// even, for codes at which fp32-subnormal inputs round to zero anyway
+// (code >= 8): V / X * 64 = V * 2^(133 - code) is exact, clamped to +-127
+// before rounding (the same result as after), and rounded by adding
+// 1.5 * 2^23, whose sum's low byte is the two's-complement code.
+__device__ __forceinline__ Pack8 int8_convert8(const uint32_t v[8], uint32_t code) {
+  const int k = 133 - (int)code;
+  uint32_t b[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    float x = __builtin_amdgcn_ldexpf(__builtin_bit_cast(float, v[i]), k);
+    x = __builtin_amdgcn_fmed3f(x, -127.0f, 127.0f);
+    b[i] = __builtin_bit_cast(uint32_t, x + 12582912.0f);
+  }
+  Pack8 o;
+  // bytes 0 of b[0..3] -> one dword: perm picks byte 0 of each source
+  o.w[0] = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u) | __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);
+  o.w[1] = __builtin_amdgcn_perm(b[5], b[4], 0x0C0C0400u) | __builtin_amdgcn_perm(b[7], b[6], 0x04000C0Cu);
+  return o;
+}
+
 // Codes of 8 elements of a block with scale `code`.  `v` holds fp32 bits;
 // `rnd` the stochastic-rounding words (ignored for RNE).
 template <int F, bool SR>
@@ -174,6 +194,7 @@ __device__ __forceinline__ Pack8 convert8(const uint32_t v[8], uint32_t code, co
   }
   if (!SR && (F == E4M3 || F == E5M2 || F == E2M1) && code >= (uint32_t)DazFree<F>::value)
     return hw_convert8<F>(v, code);
+  if (!SR && F == INT8 && code >= (uint32_t)DazFree<F>::value) return int8_convert8(v, code);
   uint32_t c[8];
 #pragma unroll
   for (int k = 0; k < 8; k++) c[k] = cvt_exact<F, SR>(v[k], code, SR ? rnd[k] : 0u);
@@ -333,8 +354,6 @@ struct QP {
   uint8_t* s_colt;
   uint64_t seed, off;
   uint32_t signs;
-  int lpr_log2;        // rows kernel: lanes per row (log2)
-  int rows_per_block;  // rows kernel
   int tiles_r, tiles_c;  // tile kernel: tiles along rows / columns
   int wpr;               // block kernel: waves per row (64 blocks each)
 };
@@ -423,58 +442,6 @@ __device__ __forceinline__ void row_chunk_bf16(const QP& p, int64_t r, int64_t c
 }
 
 // ---------------------------------------------------------------------------
-// row-wise kernel
-// ---------------------------------------------------------------------------
-template <int SRC>
-__device__ __forceinline__ void load8(const uint8_t* rowp, int64_t c, uint32_t raw[8]) {
-  if (SRC == SRC_BF16) {
-    const uint4 t = ld_stream(rowp + 16 * c);
-    raw[0] = t.x; raw[1] = t.y; raw[2] = t.z; raw[3] = t.w;
-  } else {
-    const uint4 t0 = ld_stream(rowp + 32 * c);
-    const uint4 t1 = ld_stream(rowp + 32 * c + 16);
-    raw[0] = t0.x; raw[1] = t0.y; raw[2] = t0.z; raw[3] = t0.w;
-    raw[4] = t1.x; raw[5] = t1.y; raw[6] = t1.z; raw[7] = t1.w;
-  }
-}
-
-// 8-element chunks per lane in flight per row iteration
-constexpr int ROW_UNROLL = 4;
-
-template <int SRC, int F, bool SR, bool HAD>
-__global__ __launch_bounds__(256) void k_quant_rows(QP p) {
-  const int lpr = 1 << p.lpr_log2;
-  const int tid = threadIdx.x;
-  const int lr = tid & (lpr - 1);
-  const HadLane hl = had_lane(p.signs, lr & 3);  // chunk c = lr + k lpr: c & 3 == lr & 3
-  const int rpp = 256 >> p.lpr_log2;
-  const int64_t cpr = p.cols >> 3;  // 8-element chunks per row
-  const int64_t r0 = (int64_t)blockIdx.x * p.rows_per_block;
-  const int64_t r1 = r0 + p.rows_per_block < p.rows ? r0 + p.rows_per_block : p.rows;
-  for (int64_t r = r0 + (tid >> p.lpr_log2); r < r1; r += rpp) {
-    const uint8_t* rowp = p.x + r * p.ld_bytes;
-    for (int64_t c = lr; c < cpr; c += (int64_t)lpr * ROW_UNROLL) {
-      uint32_t raw[ROW_UNROLL][8];
-#pragma unroll
-      for (int u = 0; u < ROW_UNROLL; u++)
-        if (c + u * lpr < cpr) load8<SRC>(rowp, c + u * lpr, raw[u]);
-#pragma unroll
-      for (int u = 0; u < ROW_UNROLL; u++) {
-        if (c + u * lpr < cpr) {
-          if constexpr (SRC == SRC_BF16 && !HAD && HwPath<F, SR>::value) {
-            row_chunk_bf16<F>(p, r, c + u * lpr, raw[u]);
-          } else {
-            uint32_t v[8];
-            widen8<SRC>(raw[u], v);
-            row_chunk<F, SR, HAD>(p, r, c + u * lpr, v, hl);
-          }
-        }
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // block kernel: row-wise layout with one whole block per lane
 // ---------------------------------------------------------------------------
 // Used with the Hadamard transform: all five butterfly stages then run in a
@@ -497,6 +464,9 @@ __device__ __forceinline__ void store32_stream(uint8_t* p, const Pack8 o[4]) {
 template <int SRC, int F, bool SR, bool HAD>
 __global__ __launch_bounds__(256) void k_quant_blocks(QP p) {
   constexpr int ESZ = SRC == SRC_BF16 ? 2 : 4;
+  // bf16 without SR or the transform, formats with a hardware conversion: the
+  // packed-pair path (block max and conversion on bf16 pairs)
+  constexpr bool PACKED = SRC == SRC_BF16 && !HAD && HwPath<F, SR>::value;
   const int lane = threadIdx.x & 63;
   const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t r = g / p.wpr;
@@ -504,47 +474,63 @@ __global__ __launch_bounds__(256) void k_quant_blocks(QP p) {
   const int64_t bpr = p.cols >> 5;
   if (r >= p.rows || kb >= bpr) return;  // no lane exchanges below
   const uint8_t* src = p.x + r * p.ld_bytes + kb * 32 * ESZ;
+  uint32_t raw[8 * ESZ];
+#pragma unroll
+  for (int j = 0; j < 2 * ESZ; j++) {
+    const uint4 t = *(const uint4*)(src + 16 * j);
+    raw[4 * j] = t.x; raw[4 * j + 1] = t.y; raw[4 * j + 2] = t.z; raw[4 * j + 3] = t.w;
+  }
   uint32_t v[32];
-  if (SRC == SRC_BF16) {
+  uint32_t am = 0;
+  if constexpr (PACKED) {
+    uint32_t m = 0;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const uint4 t = *(const uint4*)(src + 16 * j);
-      const uint32_t w[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        v[8 * j + 2 * i] = w[i] << 16;
-        v[8 * j + 2 * i + 1] = w[i] & 0xFFFF0000u;
-      }
-    }
+    for (int i = 0; i < 16; i++) m = pk_max_u16(m, raw[i] & 0x7FFF7FFFu);
+    am = umax(m << 16, m & 0xFFFF0000u);
   } else {
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const uint4 t = *(const uint4*)(src + 16 * j);
-      v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
+    for (int j = 0; j < 4; j++) widen8<SRC>(&raw[j * 2 * ESZ], &v[8 * j]);
+    if (HAD) {
+#pragma unroll
+      for (int k = 0; k < 32; k++) v[k] = daz32(v[k]);
+      hadamard_local(v, p.signs);
     }
-  }
-  if (HAD) {
 #pragma unroll
-    for (int k = 0; k < 32; k++) v[k] = daz32(v[k]);
-    hadamard_local(v, p.signs);
+    for (int k = 0; k < 32; k++) am = umax(am, v[k] & 0x7FFFFFFFu);
   }
-  uint32_t am = 0;
-#pragma unroll
-  for (int k = 0; k < 32; k++) am = umax(am, v[k] & 0x7FFFFFFFu);
   const uint32_t code = scale_code<F>(am);
   p.s_row[r * bpr + kb] = (uint8_t)code;
   Pack8 o[4];
+  bool fast = false;
+  if constexpr (HwPath<F, SR>::value) {
+    if (hw_ok<F>(code)) {
 #pragma unroll
-  for (int h = 0; h < 4; h++) {
-    uint32_t rnd[8];
-    if (SR) {
-      const uint64_t c = (uint64_t)(r * p.cols + kb * 32 + 8 * h) >> 2;
-      const U4 a = sr_words(p.seed, p.off, 0u, c);
-      const U4 b = sr_words(p.seed, p.off, 0u, c + 1);
-      rnd[0] = a.x; rnd[1] = a.y; rnd[2] = a.z; rnd[3] = a.w;
-      rnd[4] = b.x; rnd[5] = b.y; rnd[6] = b.z; rnd[7] = b.w;
+      for (int h = 0; h < 4; h++) {
+        if constexpr (PACKED)
+          o[h] = hw_convert8_bf16<F>(&raw[4 * h], code);
+        else
+          o[h] = hw_convert8<F>(&v[8 * h], code);
+      }
+      fast = true;
     }
-    o[h] = convert8<F, SR>(&v[8 * h], code, rnd);
+  }
+  if (!fast) {
+    if constexpr (PACKED) {
+#pragma unroll
+      for (int j = 0; j < 4; j++) widen8<SRC>(&raw[j * 2 * ESZ], &v[8 * j]);
+    }
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+      uint32_t rnd[8];
+      if (SR) {
+        const uint64_t c = (uint64_t)(r * p.cols + kb * 32 + 8 * h) >> 2;
+        const U4 a = sr_words(p.seed, p.off, 0u, c);
+        const U4 b = sr_words(p.seed, p.off, 0u, c + 1);
+        rnd[0] = a.x; rnd[1] = a.y; rnd[2] = a.z; rnd[3] = a.w;
+        rnd[4] = b.x; rnd[5] = b.y; rnd[6] = b.z; rnd[7] = b.w;
+      }
+      o[h] = convert8<F, SR>(&v[8 * h], code, rnd);
+    }
   }
   store32_stream<F>(p.q_row + r * p.qr_pitch + kb * 4 * Fmt<F>::bits, o);
 }
@@ -846,21 +832,10 @@ static QP make_qp(const QuantArgs& a) {
 template <int SRC, int F, bool SR, bool HAD>
 static hipError_t rows_launch(const QP& p0, hipStream_t st) {
   QP p = p0;
-  if constexpr (HAD) {
-    const int64_t wpr = (p.cols / 32 + 63) / 64;
-    p.wpr = (int)wpr;
-    const int64_t waves = p.rows * wpr;
-    hipLaunchKernelGGL((k_quant_blocks<SRC, F, SR, HAD>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, p);
-    return hipGetLastError();
-  }
-  const int64_t cpr = p.cols / 8;
-  int lg = 6;  // up to a wave per row
-  while (lg > 2 && ((int64_t)1 << lg) > cpr) lg--;
-  p.lpr_log2 = lg;
-  const int rpp = 256 >> lg;
-  p.rows_per_block = rpp;
-  const int64_t blocks = (p.rows + p.rows_per_block - 1) / p.rows_per_block;
-  hipLaunchKernelGGL((k_quant_rows<SRC, F, SR, HAD>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+  const int64_t wpr = (p.cols / 32 + 63) / 64;  // waves per row, 64 blocks each
+  p.wpr = (int)wpr;
+  const int64_t waves = p.rows * wpr;
+  hipLaunchKernelGGL((k_quant_blocks<SRC, F, SR, HAD>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
