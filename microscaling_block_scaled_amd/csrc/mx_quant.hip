@@ -127,6 +127,37 @@ __device__ __forceinline__ Pack8 hw_convert8_bf16(const uint32_t raw[4], uint32_
 template <int F, bool SR> struct HwPath {
   static constexpr bool value = !SR && (F == E4M3 || F == E5M2 || F == E2M1);
 };
+// ... and those whose hardware conversion takes a whole block of 32 bf16
+// elements at once (FP6, also checked bit for bit against the definition).
+template <int F, bool SR> struct HwPath32 {
+  static constexpr bool value = HwPath<F, SR>::value || (!SR && (F == E2M3 || F == E3M2));
+};
+
+// FP6 codes of a whole block of 32 bf16 elements held packed in pr[16]
+// (element 2i in the low half of pr[i]): one 32-element conversion, whose
+// 24-byte little-endian bit stream is split into the Pack8 groups.
+typedef uint32_t v16u __attribute__((ext_vector_type(16)));
+typedef __bf16 v32bf __attribute__((ext_vector_type(32)));
+typedef int v6i __attribute__((ext_vector_type(6)));
+template <int F>
+__device__ __forceinline__ void hw_convert32_bf16_fp6(const uint32_t pr[16], uint32_t code, Pack8 o[4]) {
+  const float S = __builtin_bit_cast(float, code << 23);
+  v16u t;
+#pragma unroll
+  for (int i = 0; i < 16; i++) t[i] = pr[i];
+  const v32bf in = __builtin_bit_cast(v32bf, t);
+  v6i r;
+  if (F == E2M3)
+    r = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(in, S);
+  else
+    r = __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(in, S);
+  const uint32_t d0 = (uint32_t)r[0], d1 = (uint32_t)r[1], d2 = (uint32_t)r[2];
+  const uint32_t d3 = (uint32_t)r[3], d4 = (uint32_t)r[4], d5 = (uint32_t)r[5];
+  o[0].w[0] = d0;                      o[0].w[1] = d1 & 0xFFFFu;
+  o[1].w[0] = (d1 >> 16) | (d2 << 16); o[1].w[1] = d2 >> 16;
+  o[2].w[0] = d3;                      o[2].w[1] = d4 & 0xFFFFu;
+  o[3].w[0] = (d4 >> 16) | (d5 << 16); o[3].w[1] = d5 >> 16;
+}
 // Whether a block with scale `code` can take the hardware conversion.
 template <int F>
 __device__ __forceinline__ bool hw_ok(uint32_t code) {
@@ -466,7 +497,7 @@ __global__ __launch_bounds__(256) void k_quant_blocks(QP p) {
   constexpr int ESZ = SRC == SRC_BF16 ? 2 : 4;
   // bf16 without SR or the transform, formats with a hardware conversion: the
   // packed-pair path (block max and conversion on bf16 pairs)
-  constexpr bool PACKED = SRC == SRC_BF16 && !HAD && HwPath<F, SR>::value;
+  constexpr bool PACKED = SRC == SRC_BF16 && !HAD && HwPath32<F, SR>::value;
   const int lane = threadIdx.x & 63;
   const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t r = g / p.wpr;
@@ -502,7 +533,12 @@ __global__ __launch_bounds__(256) void k_quant_blocks(QP p) {
   p.s_row[r * bpr + kb] = (uint8_t)code;
   Pack8 o[4];
   bool fast = false;
-  if constexpr (HwPath<F, SR>::value) {
+  if constexpr (PACKED && (F == E2M3 || F == E3M2)) {
+    if (hw_ok<F>(code)) {
+      hw_convert32_bf16_fp6<F>(raw, code, o);
+      fast = true;
+    }
+  } else if constexpr (HwPath<F, SR>::value) {
     if (hw_ok<F>(code)) {
 #pragma unroll
       for (int h = 0; h < 4; h++) {
@@ -670,13 +706,15 @@ __device__ __forceinline__ void col_pair_bf16(const QP& p, const uint32_t w[32],
     const uint32_t code = codes[k];
     Pack8 o[4];
     if (hw_ok<F>(code)) {
+      uint32_t pr[16];  // rows 2 j, 2 j + 1 of this column
 #pragma unroll
-      for (int h = 0; h < 4; h++) {
-        uint32_t pr[4];  // rows 8 h + 2 j, 8 h + 2 j + 1 of this column
+      for (int j = 0; j < 16; j++)
+        pr[j] = __builtin_amdgcn_perm(w[2 * j + 1], w[2 * j], k == 0 ? 0x05040100u : 0x07060302u);
+      if constexpr (F == E2M3 || F == E3M2) {
+        hw_convert32_bf16_fp6<F>(pr, code, o);
+      } else {
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-          pr[j] = __builtin_amdgcn_perm(w[8 * h + 2 * j + 1], w[8 * h + 2 * j], k == 0 ? 0x05040100u : 0x07060302u);
-        o[h] = hw_convert8_bf16<F>(pr, code);
+        for (int h = 0; h < 4; h++) o[h] = hw_convert8_bf16<F>(&pr[4 * h], code);
       }
     } else {
       uint32_t v[32], rnd[8];
@@ -713,6 +751,7 @@ __global__ __launch_bounds__(256) void k_quant_tiles(QP p) {
   // whole bf16 tiles with rows of s_row in whole dwords: the row-wise scales
   // are gathered in LDS and written one dword per row
   constexpr bool FAST = SRC == SRC_BF16 && !HAD && HwPath<F, SR>::value;
+  constexpr bool FASTCOL = SRC == SRC_BF16 && !HAD && HwPath32<F, SR>::value;
   const bool gather = FAST && ROWS && whole && (p.cols & 127) == 0;
   const int cq = tid % T::CPRW, sub = tid / T::CPRW;
   const HadLane hl = had_lane(p.signs, cq & 3);  // tile columns start at a multiple of 4 chunks
@@ -777,7 +816,7 @@ __global__ __launch_bounds__(256) void k_quant_tiles(QP p) {
     uint32_t w[32];
 #pragma unroll
     for (int i = 0; i < 32; i++) w[i] = *(const uint32_t*)(src + i * T::ROWB);
-    if constexpr (FAST) {
+    if constexpr (FASTCOL) {
       col_pair_bf16<F>(p, w, c0 + 2 * d, r0, qb);
     } else {
 #pragma unroll
