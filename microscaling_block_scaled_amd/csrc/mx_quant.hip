@@ -353,9 +353,13 @@ __device__ __forceinline__ void hadamard_quad(uint32_t v[8], const HadLane& hl) 
 
 // Whole block in one lane.
 __device__ __forceinline__ void hadamard_local(uint32_t v[32], uint32_t signs) {
+  if (signs) {  // wave-uniform: the plain Sylvester matrix skips the flips
+#pragma unroll
+    for (int k = 0; k < 32; k++) v[k] ^= ((signs >> k) & 1u) << 31;
+  }
   float f[32];
 #pragma unroll
-  for (int k = 0; k < 32; k++) f[k] = __builtin_bit_cast(float, v[k] ^ (((signs >> k) & 1u) << 31));
+  for (int k = 0; k < 32; k++) f[k] = __builtin_bit_cast(float, v[k]);
 #pragma unroll
   for (int h = 1; h < 32; h <<= 1) {
 #pragma unroll
@@ -519,11 +523,25 @@ __global__ __launch_bounds__(256) void k_quant_blocks(QP p) {
     for (int i = 0; i < 16; i++) m = pk_max_u16(m, raw[i] & 0x7FFF7FFFu);
     am = umax(m << 16, m & 0xFFFF0000u);
   } else {
+    // Flush subnormal inputs before the transform.  For bf16 a block is first
+    // checked on the packed pairs (magnitude - 1 wraps for zero, lands below
+    // 0x7F only for a subnormal), and only lanes holding one flush.
+    bool sub = true;
+    if constexpr (SRC == SRC_BF16 && HAD) {
+      u16x2 mn = {0xFFFF, 0xFFFF};
+      const u16x2 one = {1, 1};
+#pragma unroll
+      for (int i = 0; i < 16; i++)
+        mn = __builtin_elementwise_min(mn, __builtin_bit_cast(u16x2, raw[i] & 0x7FFF7FFFu) - one);
+      sub = mn.x < 0x7F || mn.y < 0x7F;
+    }
 #pragma unroll
     for (int j = 0; j < 4; j++) widen8<SRC>(&raw[j * 2 * ESZ], &v[8 * j]);
     if (HAD) {
+      if (sub) {
 #pragma unroll
-      for (int k = 0; k < 32; k++) v[k] = daz32(v[k]);
+        for (int k = 0; k < 32; k++) v[k] = daz32(v[k]);
+      }
       hadamard_local(v, p.signs);
     }
 #pragma unroll
