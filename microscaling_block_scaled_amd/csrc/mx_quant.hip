@@ -479,17 +479,18 @@ __device__ __forceinline__ void row_chunk_bf16(const QP& p, int64_t r, int64_t c
 // ---------------------------------------------------------------------------
 // block kernel: row-wise layout with one whole block per lane
 // ---------------------------------------------------------------------------
-// Used with the Hadamard transform: all five butterfly stages then run in a
-// lane's registers (no lane exchanges), and the block max needs no reduction
-// across lanes.  Wave g of the grid takes 64 consecutive blocks of row
-// g / wpr; a lane reads its block's 64 (bf16) or 128 (fp32) bytes and writes
-// its packed codes as one run.
+// All five butterfly stages of the transform run in a lane's registers (no
+// lane exchanges), and the block max needs no reduction across lanes.  Wave g
+// of the grid takes 64 consecutive blocks of row g / wpr; a lane reads its
+// block's 64 (bf16) or 128 (fp32) bytes and writes its packed codes as one run.
+
+// A lane's run of codes: FP4's 16 bytes go out as one streaming store; 8-bit
+// and FP6 runs take two or three stores each, whose pieces interleave with the
+// neighbouring lanes', so they are ordinary stores that the L2 assembles into
+// whole lines.
 template <int F>
 __device__ __forceinline__ void store32_stream(uint8_t* p, const Pack8 o[4]) {
-  if (Fmt<F>::bits == 8) {
-    st_stream(p, make_uint4(o[0].w[0], o[0].w[1], o[1].w[0], o[1].w[1]));
-    st_stream(p + 16, make_uint4(o[2].w[0], o[2].w[1], o[3].w[0], o[3].w[1]));
-  } else if (Fmt<F>::bits == 4) {
+  if (Fmt<F>::bits == 4) {
     st_stream(p, make_uint4(o[0].w[0], o[1].w[0], o[2].w[0], o[3].w[0]));
   } else {
     store32<F>(p, o);
