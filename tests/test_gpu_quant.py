@@ -64,7 +64,11 @@ def exhaustive_bf16_blocks():
     leading element that sets the block scale, over many scale exponents."""
     pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     rows = []
-    for s in (-133, -126, -120, -100, -60, -20, -9, -3, 0, 2, 5, 9, 20, 60, 100, 120, 126):
+    # the scale exponents include both sides of each format's smallest scale at
+    # which fp32-subnormal inputs round to zero anyway (where the kernels switch
+    # from the exact integer conversion to the hardware or float one)
+    for s in (-133, -126, -123, -122, -121, -120, -119, -118, -117, -109, -108, -100, -95, -94,
+              -60, -20, -9, -3, 0, 2, 5, 9, 20, 60, 100, 120, 126):
         lead = np.float32(2.0 ** s) if s > -127 else np.float32(0.0)
         lead_bits = np.frombuffer(np.float32(lead).tobytes(), np.uint32)[0] >> 16
         perm = np.random.default_rng(s + 200).permutation(pats)
@@ -86,6 +90,7 @@ def test_exhaustive_bf16_patterns(mx, oracle, fmt):
     for rnd in (0, 1):
         run_both(mx, oracle, x, fmt, 1, rnd, seed=123456789, off=3, what="exhaustive rows")
     run_both(mx, oracle, x, fmt, 2, 0, what="exhaustive cols")
+    run_both(mx, oracle, x, fmt, 3, 0, what="exhaustive dual")
 
 
 def test_dual_layout_e4m3(mx, oracle):
