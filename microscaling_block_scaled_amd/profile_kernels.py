@@ -141,13 +141,24 @@ def traffic(fetch_dir: str, write_dir: str, out: str) -> None:
 
 
 def stats(trace_dir: str, out: str, cmd: str) -> None:
+    """The --stats table, plus each kernel's average over its later half of
+    calls (in dispatch order): the clock needs some milliseconds of load to
+    settle, so the first calls of a run are slower than the steady state."""
     rows = _rows(trace_dir, "*kernel_stats.csv")
+    late: dict[str, list[float]] = {}
+    for r in sorted(_rows(trace_dir, "*kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"])):
+        late.setdefault(r["Kernel_Name"], []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     lines = [f"Command: `{cmd}`", "",
-             "| kernel | calls | avg us | min us | max us | total % |", "|---|---|---|---|---|---|"]
+             "| kernel | calls | avg us | min us | max us | later-half avg us | total % |",
+             "|---|---|---|---|---|---|---|"]
     for r in rows:
         name = r["Name"].split("(")[0]
+        d = late.get(r["Name"], [])
+        half = d[len(d) // 2:]
+        lh = f"{sum(half) / len(half):.2f}" if half else "-"
         lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {lh} | "
                      f"{float(r['Percentage']):.1f} |")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
