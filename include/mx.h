@@ -142,6 +142,28 @@ int mx_gemm(const void* a_q, const uint8_t* a_s, int32_t a_fmt, const void* b_q,
             const uint8_t* b_s, int32_t b_fmt, int64_t M, int64_t N, int64_t K, float* c,
             int64_t ldc, mx_stream_t stream);
 
+/*
+ * mx_gemm_mx -- the product of mx_gemm written straight out in MX format:
+ * each fp32 row block C[m, 32 j .. 32 j + 31] is quantized as Algorithm 1 of
+ * the MX summary (section 3) does it -- shared scale from the block max,
+ * elements rounded to nearest even, saturated -- inside the GEMM's epilogue,
+ * the producer-side quantization of "Format-Aware Fusion for Fast FP4
+ * Pretraining".  The codes and scales are the ones mx_quantize (row layout,
+ * fp32 source, MX_RNE, no transform) gives for the fp32 C that mx_gemm
+ * computes; the fp32 C itself is never written.
+ *   a_q .. K   as for mx_gemm.
+ *   c_fmt      MX_E4M3, MX_E5M2 or MX_E2M1 (others: MX_ERR_UNSUPPORTED).
+ *   c_q        [M x N] packed codes, row pitch N * bits / 8, 16-byte aligned.
+ *   c_s        [M x N/32] scales.
+ * N % 32 == 0 and K % 32 == 0 (MX_ERR_SHAPE).  The fused epilogue lives in
+ * the staged MFMA kernel only: it needs K a positive multiple of 512, 16-byte aligned scale
+ * arrays and operands under 4 GiB; outside that the call returns
+ * MX_ERR_UNSUPPORTED and writes nothing.  M == 0 or N == 0 writes nothing.
+ */
+int mx_gemm_mx(const void* a_q, const uint8_t* a_s, int32_t a_fmt, const void* b_q,
+               const uint8_t* b_s, int32_t b_fmt, int64_t M, int64_t N, int64_t K,
+               int32_t c_fmt, void* c_q, uint8_t* c_s, mx_stream_t stream);
+
 /* Host-only helpers: bytes of a packed [rows x cols] element array (blocks
  * along cols) and of its scale array; -1 on a bad argument. */
 int64_t mx_packed_bytes(int32_t fmt, int64_t rows, int64_t cols);

@@ -109,8 +109,25 @@ int mx_gemm(const void* a_q, const uint8_t* a_s, int32_t a_fmt, const void* b_q,
   if (!c) return MX_ERR_ARG;
   if (K > 0 && (!a_q || !a_s || !b_q || !b_s)) return MX_ERR_ARG;
   if (K > 0 && (!aligned16(a_q) || !aligned16(b_q))) return MX_ERR_ALIGN;
-  return hip_status(
-      mx::launch_gemm(a_q, a_s, a_fmt, b_q, b_s, b_fmt, M, N, K, c, ldc, (hipStream_t)stream));
+  return hip_status(mx::launch_gemm(a_q, a_s, a_fmt, b_q, b_s, b_fmt, M, N, K, c, ldc, -1, nullptr,
+                                    nullptr, (hipStream_t)stream));
+}
+
+int mx_gemm_mx(const void* a_q, const uint8_t* a_s, int32_t a_fmt, const void* b_q,
+               const uint8_t* b_s, int32_t b_fmt, int64_t M, int64_t N, int64_t K,
+               int32_t c_fmt, void* c_q, uint8_t* c_s, mx_stream_t stream) {
+  if (!fmt_ok(a_fmt) || !fmt_ok(b_fmt) || !fmt_ok(c_fmt)) return MX_ERR_ARG;
+  if (a_fmt == MX_INT8 || b_fmt == MX_INT8) return MX_ERR_UNSUPPORTED;
+  if (c_fmt != MX_E4M3 && c_fmt != MX_E5M2 && c_fmt != MX_E2M1) return MX_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || K < 0) return MX_ERR_ARG;
+  if (K % 32 || N % 32) return MX_ERR_SHAPE;
+  if (M == 0 || N == 0) return MX_OK;
+  if (!c_q || !c_s) return MX_ERR_ARG;
+  if (!a_q || !a_s || !b_q || !b_s) return MX_ERR_ARG;
+  if (!aligned16(a_q) || !aligned16(b_q) || !aligned16(c_q)) return MX_ERR_ALIGN;
+  const hipError_t e = mx::launch_gemm(a_q, a_s, a_fmt, b_q, b_s, b_fmt, M, N, K, nullptr, N, c_fmt,
+                                       (uint8_t*)c_q, c_s, (hipStream_t)stream);
+  return e == hipErrorNotSupported ? MX_ERR_UNSUPPORTED : hip_status(e);
 }
 
 }  // extern "C"

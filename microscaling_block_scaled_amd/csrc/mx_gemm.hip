@@ -24,6 +24,7 @@
 // Result: lane l holds C rows 4 (l / 16) + v, v = 0..3, column l % 16.
 #include <utility>
 
+#include "mx_convert.hpp"
 #include "mx_device.hpp"
 #include "mx_internal.h"
 
@@ -434,6 +435,84 @@ __device__ __forceinline__ void substep(v16f (&acc)[4][4], const Ops& cur, Slot&
   });
 }
 
+// MX output of the product: C row-wise in MX format, blocks of 32 along N
+// (Algorithm 1 of the MX summary, section 3, applied to each fp32 block of the
+// product, round to nearest even), as "Format-Aware Fusion for Fast FP4
+// Pretraining" fuses the quantization into the producer.
+struct MxOut {
+  int fmt;         // E4M3, E5M2 or E2M1; negative: fp32 C
+  uint8_t* q;      // [M x N] packed codes, row pitch N * bits / 8
+  uint8_t* s;      // [M x N/32] scales
+};
+
+// A wave's 128 x 128 piece (rows r0.., columns c0.., c0 % 32 == 0) as MX
+// blocks: the 32 columns of acc[i][j] for row 32 i + l % 32 are one block,
+// held half by lane l (columns 8 q + e) and half by lane l ^ 32 (8 q + 4 + e).
+// The block max and the codes' halves are exchanged between the two lanes, so
+// each lane stores 16 consecutive columns' codes in one piece.
+template <int F>
+__device__ __forceinline__ void store_mx(const v16f (&acc)[4][4], const MxOut& mo, int64_t r0, int64_t c0,
+                                         int64_t M, int64_t N, int lane) {
+  constexpr int bits = Fmt<F>::bits;
+  const int lr = lane & 31, hi = lane >> 5;
+  const int partner = (lane ^ 32) << 2;
+  const int64_t nb = N >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int64_t row = r0 + 32 * i + lr;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const v16f& t = acc[i][j];
+      uint32_t v[16];
+      uint32_t am = 0;
+#pragma unroll
+      for (int k = 0; k < 16; k++) {
+        // the element is read into a scalar first: a bit cast applied
+        // directly to a vector-element expression reads element 0
+        const float e = t[k];
+        v[k] = __builtin_bit_cast(uint32_t, e);
+        am = umax(am, v[k] & 0x7FFFFFFFu);
+      }
+      am = umax(am, (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)am));
+      const uint32_t code = scale_code<F>(am);
+      uint32_t rnd[8];
+      // codes of this lane's columns: groups q = 0..3 of four, at 8 q + 4 hi
+      const Pack8 p0 = convert8<F, false>(&v[0], code, rnd);  // groups 0, 1
+      const Pack8 p1 = convert8<F, false>(&v[8], code, rnd);  // groups 2, 3
+      const int64_t blk = (c0 >> 5) + j;
+      const bool live = row < M && blk < nb;
+      if (bits == 8) {
+        // group dwords g[q]; the low lane keeps groups 0-1 of both lanes
+        // (columns 0-15), the high lane groups 2-3 (columns 16-31)
+        const uint32_t g0 = p0.w[0], g1 = p0.w[1], g2 = p1.w[0], g3 = p1.w[1];
+        // the values to send are fixed in registers before the exchanges, so
+        // the per-lane choice cannot become branches around them
+        uint32_t s1 = hi ? g0 : g2, s2 = hi ? g1 : g3;
+        asm volatile("" : "+v"(s1), "+v"(s2));
+        const uint32_t r1 = (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)s1);
+        const uint32_t r2 = (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)s2);
+        const uint4 o = hi ? make_uint4(r1, g2, r2, g3) : make_uint4(g0, r1, g1, r2);
+        if (live) *(uint4*)(mo.q + row * N + 32 * blk + 16 * hi) = o;
+      } else {  // E2M1: group q is 16 bits (p0: groups 0 | 1 << 16, p1: 2 | 3 << 16)
+        uint32_t s1 = hi ? p0.w[0] : p1.w[0];
+        asm volatile("" : "+v"(s1));
+        const uint32_t r = (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)s1);
+        const uint32_t own = hi ? p1.w[0] : p0.w[0];
+        uint2 o;
+        if (hi) {  // columns 16-31: groups 2 (partner, own), 3 (partner, own)
+          o.x = (r & 0xFFFFu) | (own << 16);
+          o.y = (r >> 16) | (own & 0xFFFF0000u);
+        } else {  // columns 0-15: groups 0 (own, partner), 1 (own, partner)
+          o.x = (own & 0xFFFFu) | (r << 16);
+          o.y = (own >> 16) | (r & 0xFFFF0000u);
+        }
+        if (live) *(uint2*)(mo.q + row * (N >> 1) + 16 * blk + 8 * hi) = o;
+      }
+      if (live && hi == 0) mo.s[row * nb + blk] = (uint8_t)code;
+    }
+  }
+}
+
 template <int FA, int FB, int KS>
 __global__ __launch_bounds__(256) void k_gemm_fast(const uint8_t* __restrict__ aq,
                                                    const uint8_t* __restrict__ as,
@@ -441,7 +520,7 @@ __global__ __launch_bounds__(256) void k_gemm_fast(const uint8_t* __restrict__ a
                                                    const uint8_t* __restrict__ bs, int64_t M,
                                                    int64_t N, int64_t K, float* __restrict__ c,
                                                    int64_t ldc, int tiles_m, int tiles_n,
-                                                   int vec_store) {
+                                                   int vec_store, MxOut mo) {
   using C = Fast<FA, FB, KS>;
   constexpr int NST = C::NST, SUB = C::SUB, SPC = C::SPC;
   constexpr int SEGS = C::CHA + C::CHB;  // 1 KB panel segments per wave per stage
@@ -613,6 +692,14 @@ __global__ __launch_bounds__(256) void k_gemm_fast(const uint8_t* __restrict__ a
 
   // acc[i][j] is the 32 x 32 tile C^T[n][m]: lane l holds, for v = 4q + e,
   // C[m0 + wm*128 + 32 i + l % 32][n0 + wn*128 + 32 j + 8 q + 4 (l / 32) + e]
+  if (mo.fmt >= 0) {  // wave-uniform: MX output
+    switch (mo.fmt) {
+      case E4M3: store_mx<E4M3>(acc, mo, m0 + wm * 128, n0 + wn * 128, M, N, lane); break;
+      case E5M2: store_mx<E5M2>(acc, mo, m0 + wm * 128, n0 + wn * 128, M, N, lane); break;
+      default: store_mx<E2M1>(acc, mo, m0 + wm * 128, n0 + wn * 128, M, N, lane); break;
+    }
+    return;
+  }
   const int lr = lane & 31;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
@@ -640,18 +727,18 @@ __global__ __launch_bounds__(256) void k_gemm_fast(const uint8_t* __restrict__ a
 template <int FA, int FB, int KS>
 static hipError_t launch_fast(const void* aq, const uint8_t* as, const void* bq, const uint8_t* bs,
                               int64_t M, int64_t N, int64_t K, float* c, int64_t ldc,
-                              int64_t tiles_m, int64_t tiles_n, hipStream_t st) {
+                              int64_t tiles_m, int64_t tiles_n, const MxOut& mo, hipStream_t st) {
   const int vec = ((uintptr_t)c % 16) == 0 && ldc % 4 == 0;
   hipLaunchKernelGGL((k_gemm_fast<FA, FB, KS>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
                      st, (const uint8_t*)aq, as, (const uint8_t*)bq, bs, M, N, K, c, ldc,
-                     (int)tiles_m, (int)tiles_n, vec);
+                     (int)tiles_m, (int)tiles_n, vec, mo);
   return hipGetLastError();
 }
 
 template <int FA, int FB>
 static hipError_t gemm_launch(const void* aq, const uint8_t* as, const void* bq, const uint8_t* bs,
                               int64_t M, int64_t N, int64_t K, float* c, int64_t ldc,
-                              hipStream_t st) {
+                              const MxOut& mo, hipStream_t st) {
   const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   // The fast path addresses operands and scales with 32-bit buffer offsets
   // (rows rounded up to whole tiles, plus the reach of the last chunk, stay
@@ -666,10 +753,11 @@ static hipError_t gemm_launch(const void* aq, const uint8_t* as, const void* bq,
                     tiles_m * tiles_n < ((int64_t)1 << 31);
   if (fast) {
     if constexpr (Fmt<FA>::bits == 4 && Fmt<FB>::bits == 4)
-      return launch_fast<FA, FB, 256>(aq, as, bq, bs, M, N, K, c, ldc, tiles_m, tiles_n, st);
+      return launch_fast<FA, FB, 256>(aq, as, bq, bs, M, N, K, c, ldc, tiles_m, tiles_n, mo, st);
     else
-      return launch_fast<FA, FB, 128>(aq, as, bq, bs, M, N, K, c, ldc, tiles_m, tiles_n, st);
+      return launch_fast<FA, FB, 128>(aq, as, bq, bs, M, N, K, c, ldc, tiles_m, tiles_n, mo, st);
   }
+  if (mo.fmt >= 0) return hipErrorNotSupported;  // MX output: the staged kernel only
   using L = GemmLds<FA, FB>;
   static bool attr_done = false;  // benign race: the call is idempotent
   if (!attr_done) {
@@ -686,9 +774,10 @@ static hipError_t gemm_launch(const void* aq, const uint8_t* as, const void* bq,
 
 hipError_t launch_gemm(const void* aq, const uint8_t* as, int fa, const void* bq,
                        const uint8_t* bs, int fb, int64_t M, int64_t N, int64_t K, float* c,
-                       int64_t ldc, hipStream_t st) {
+                       int64_t ldc, int out_fmt, uint8_t* out_q, uint8_t* out_s, hipStream_t st) {
+  const MxOut mo{out_fmt, out_q, out_s};
 #define MX_G(A, B) \
-  if (fa == A && fb == B) return gemm_launch<A, B>(aq, as, bq, bs, M, N, K, c, ldc, st);
+  if (fa == A && fb == B) return gemm_launch<A, B>(aq, as, bq, bs, M, N, K, c, ldc, mo, st);
 #define MX_GA(A) MX_G(A, E4M3) MX_G(A, E5M2) MX_G(A, E2M3) MX_G(A, E3M2) MX_G(A, E2M1)
   MX_GA(E4M3) MX_GA(E5M2) MX_GA(E2M3) MX_GA(E3M2) MX_GA(E2M1)
 #undef MX_GA

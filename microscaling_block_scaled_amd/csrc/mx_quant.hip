@@ -21,6 +21,7 @@
 //                  columns (two bf16 or one fp32).  On whole tiles the four
 //                  blocks of a column sit in one lane quad, which writes the
 //                  column's transposed line in 64-byte runs.
+#include "mx_convert.hpp"
 #include "mx_device.hpp"
 #include "mx_internal.h"
 
@@ -29,209 +30,6 @@
 namespace mx {
 
 enum { SRC_F32 = 0, SRC_BF16 = 1 };
-typedef short v2s __attribute__((ext_vector_type(2)));
-
-// ---------------------------------------------------------------------------
-// conversion of 8 elements of one block to packed codes
-// ---------------------------------------------------------------------------
-// Packed result of 8 elements: FP8 / INT8 8 bytes in w[0..1]; FP6 48 bits (w[0]
-// then the low 16 bits of w[1]); FP4 32 bits in w[0].
-struct Pack8 { uint32_t w[2]; };
-
-// gfx950's scaled conversions divide by the scale and round to nearest even.
-// For E4M3, E5M2 and E2M1 they agree bit for bit with the definition on every
-// finite non-subnormal input, except that FP8 overflow gives the NaN / Inf code
-// instead of saturating; fix_sat repairs that.  Used only for scale codes at
-// which fp32-subnormal inputs round to zero anyway (DazFree), so no flush is
-// needed first.
-template <int F>
-__device__ __forceinline__ uint32_t fix_sat(uint32_t r) {
-  if (F == E4M3) {  // 0x7F / 0xFF (NaN) -> 0x7E / 0xFE
-    const uint32_t t = r & 0x7F7F7F7Fu;
-    return r - (((t + 0x01010101u) & 0x80808080u) >> 7);
-  } else {  // E5M2: 0x7C / 0xFC (Inf) -> 0x7B / 0xFB
-    const uint32_t t = (r & 0x7F7F7F7Fu) ^ 0x7C7C7C7Cu;
-    const uint32_t nz = (((t & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | t) & 0x80808080u;
-    return r - ((~nz & 0x80808080u) >> 7);
-  }
-}
-
-template <int F>
-__device__ __forceinline__ Pack8 hw_convert8(const uint32_t v[8], uint32_t code) {
-  const float S = __builtin_bit_cast(float, code << 23);  // 2^(code - 127), code >= 1
-  float f[8];
-#pragma unroll
-  for (int k = 0; k < 8; k++) f[k] = __builtin_bit_cast(float, v[k]);
-  Pack8 o;
-  if (F == E4M3 || F == E5M2) {
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-      v2s t = {0, 0};
-      if (F == E4M3) {
-        t = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(t, f[4 * h], f[4 * h + 1], S, false);
-        t = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(t, f[4 * h + 2], f[4 * h + 3], S, true);
-      } else {
-        t = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(t, f[4 * h], f[4 * h + 1], S, false);
-        t = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(t, f[4 * h + 2], f[4 * h + 3], S, true);
-      }
-      o.w[h] = fix_sat<F>(__builtin_bit_cast(uint32_t, t));
-    }
-  } else {  // E2M1: saturates in hardware
-    uint32_t r = 0;
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[0], f[1], S, 0);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[2], f[3], S, 1);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[4], f[5], S, 2);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[6], f[7], S, 3);
-    o.w[0] = r;
-    o.w[1] = 0;
-  }
-  return o;
-}
-
-// The same conversion of 8 bf16 elements held packed in raw[4] (element 2i in
-// the low half of raw[i]), through the packed-bf16 form of the instructions;
-// bf16 widens to fp32 exactly, so the codes are the same.
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-template <int F>
-__device__ __forceinline__ Pack8 hw_convert8_bf16(const uint32_t raw[4], uint32_t code) {
-  const float S = __builtin_bit_cast(float, code << 23);
-  Pack8 o;
-  if (F == E4M3 || F == E5M2) {
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-      const v2bf a = __builtin_bit_cast(v2bf, raw[2 * h]), b = __builtin_bit_cast(v2bf, raw[2 * h + 1]);
-      v2s t = {0, 0};
-      if (F == E4M3) {
-        t = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(t, a, S, false);
-        t = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(t, b, S, true);
-      } else {
-        t = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(t, a, S, false);
-        t = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(t, b, S, true);
-      }
-      o.w[h] = fix_sat<F>(__builtin_bit_cast(uint32_t, t));
-    }
-  } else {  // E2M1
-    uint32_t r = 0;
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf, raw[0]), S, 0);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf, raw[1]), S, 1);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf, raw[2]), S, 2);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf, raw[3]), S, 3);
-    o.w[0] = r;
-    o.w[1] = 0;
-  }
-  return o;
-}
-
-// Formats with a hardware conversion that matches the definition (round to
-// nearest even only).
-template <int F, bool SR> struct HwPath {
-  static constexpr bool value = !SR && (F == E4M3 || F == E5M2 || F == E2M1);
-};
-// ... and those whose hardware conversion takes a whole block of 32 bf16
-// elements at once (FP6, also checked bit for bit against the definition).
-template <int F, bool SR> struct HwPath32 {
-  static constexpr bool value = HwPath<F, SR>::value || (!SR && (F == E2M3 || F == E3M2));
-};
-
-// FP6 codes of a whole block of 32 bf16 elements held packed in pr[16]
-// (element 2i in the low half of pr[i]): one 32-element conversion, whose
-// 24-byte little-endian bit stream is split into the Pack8 groups.
-typedef uint32_t v16u __attribute__((ext_vector_type(16)));
-typedef __bf16 v32bf __attribute__((ext_vector_type(32)));
-typedef int v6i __attribute__((ext_vector_type(6)));
-template <int F>
-__device__ __forceinline__ void hw_convert32_bf16_fp6(const uint32_t pr[16], uint32_t code, Pack8 o[4]) {
-  const float S = __builtin_bit_cast(float, code << 23);
-  v16u t;
-#pragma unroll
-  for (int i = 0; i < 16; i++) t[i] = pr[i];
-  const v32bf in = __builtin_bit_cast(v32bf, t);
-  v6i r;
-  if (F == E2M3)
-    r = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(in, S);
-  else
-    r = __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(in, S);
-  const uint32_t d0 = (uint32_t)r[0], d1 = (uint32_t)r[1], d2 = (uint32_t)r[2];
-  const uint32_t d3 = (uint32_t)r[3], d4 = (uint32_t)r[4], d5 = (uint32_t)r[5];
-  o[0].w[0] = d0;                      o[0].w[1] = d1 & 0xFFFFu;
-  o[1].w[0] = (d1 >> 16) | (d2 << 16); o[1].w[1] = d2 >> 16;
-  o[2].w[0] = d3;                      o[2].w[1] = d4 & 0xFFFFu;
-  o[3].w[0] = (d4 >> 16) | (d5 << 16); o[3].w[1] = d5 >> 16;
-}
-// Whether a block with scale `code` can take the hardware conversion.
-template <int F>
-__device__ __forceinline__ bool hw_ok(uint32_t code) {
-  return code >= (uint32_t)DazFree<F>::value && code != 0xFFu;
-}
-
-// Largest magnitude of the bf16 pairs in w[0 .. n-1], per half: packed 16-bit
-// unsigned max of the sign-cleared pairs (a magnitude compare for bf16).
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
-                                                                __builtin_bit_cast(u16x2, b)));
-}
-
-template <int F>
-__device__ __forceinline__ Pack8 pack8(const uint32_t c[8]) {
-  Pack8 o;
-  if (Fmt<F>::bits == 8) {
-    o.w[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    o.w[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-  } else if (Fmt<F>::bits == 4) {
-    uint32_t r = 0;
-#pragma unroll
-    for (int k = 0; k < 8; k++) r |= c[k] << (4 * k);
-    o.w[0] = r;
-    o.w[1] = 0;
-  } else {  // 6 bits, element k at bit 6k
-    o.w[0] = c[0] | (c[1] << 6) | (c[2] << 12) | (c[3] << 18) | (c[4] << 24) | (c[5] << 30);
-    o.w[1] = (c[5] >> 2) | (c[6] << 4) | (c[7] << 10);
-  }
-  return o;
-}
-
-// INT8 codes of 8 elements (fp32 bits) with scale `code`, round to nearest
-// even, for codes at which fp32-subnormal inputs round to zero anyway
-// (code >= 8): V / X * 64 = V * 2^(133 - code) is exact, clamped to +-127
-// before rounding (the same result as after), and rounded by adding
-// 1.5 * 2^23, whose sum's low byte is the two's-complement code.
-__device__ __forceinline__ Pack8 int8_convert8(const uint32_t v[8], uint32_t code) {
-  const int k = 133 - (int)code;
-  uint32_t b[8];
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    float x = __builtin_amdgcn_ldexpf(__builtin_bit_cast(float, v[i]), k);
-    x = __builtin_amdgcn_fmed3f(x, -127.0f, 127.0f);
-    b[i] = __builtin_bit_cast(uint32_t, x + 12582912.0f);
-  }
-  Pack8 o;
-  // bytes 0 of b[0..3] -> one dword: perm picks byte 0 of each source
-  o.w[0] = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u) | __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);
-  o.w[1] = __builtin_amdgcn_perm(b[5], b[4], 0x0C0C0400u) | __builtin_amdgcn_perm(b[7], b[6], 0x04000C0Cu);
-  return o;
-}
-
-// Codes of 8 elements of a block with scale `code`.  `v` holds fp32 bits;
-// `rnd` the stochastic-rounding words (ignored for RNE).
-template <int F, bool SR>
-__device__ __forceinline__ Pack8 convert8(const uint32_t v[8], uint32_t code, const uint32_t rnd[8]) {
-  if (code == 0xFFu) {  // NaN scale: NaN elements where the format has them
-    const uint32_t n = (uint32_t)Fmt<F>::nan;
-    uint32_t c[8];
-#pragma unroll
-    for (int k = 0; k < 8; k++) c[k] = n;
-    return pack8<F>(c);
-  }
-  if (!SR && (F == E4M3 || F == E5M2 || F == E2M1) && code >= (uint32_t)DazFree<F>::value)
-    return hw_convert8<F>(v, code);
-  if (!SR && F == INT8 && code >= (uint32_t)DazFree<F>::value) return int8_convert8(v, code);
-  uint32_t c[8];
-#pragma unroll
-  for (int k = 0; k < 8; k++) c[k] = cvt_exact<F, SR>(v[k], code, SR ? rnd[k] : 0u);
-  return pack8<F>(c);
-}
-
 // ---------------------------------------------------------------------------
 // streaming global accesses: every input byte is read once, and the row-wise
 // output is written in whole contiguous runs, so these bypass cache residency
@@ -504,9 +302,11 @@ __global__ __launch_bounds__(256) void k_quant_blocks(QP p) {
   // packed-pair path (block max and conversion on bf16 pairs)
   constexpr bool PACKED = SRC == SRC_BF16 && !HAD && HwPath32<F, SR>::value;
   const int lane = threadIdx.x & 63;
-  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t r = g / p.wpr;
-  const int64_t kb = (g % p.wpr) * 64 + lane;  // block of row r
+  // wave-uniform 32-bit index arithmetic (the host keeps rows * wpr < 2^32)
+  const uint32_t g = blockIdx.x * 4u + (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t wpr = (uint32_t)p.wpr;
+  const int64_t r = g / wpr;
+  const int64_t kb = (int64_t)(g % wpr) * 64 + lane;  // block of row r
   const int64_t bpr = p.cols >> 5;
   if (r >= p.rows || kb >= bpr) return;  // no lane exchanges below
   const uint8_t* src = p.x + r * p.ld_bytes + kb * 32 * ESZ;
@@ -893,6 +693,7 @@ static hipError_t rows_launch(const QP& p0, hipStream_t st) {
   const int64_t wpr = (p.cols / 32 + 63) / 64;  // waves per row, 64 blocks each
   p.wpr = (int)wpr;
   const int64_t waves = p.rows * wpr;
+  if (waves >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_quant_blocks<SRC, F, SR, HAD>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, p);
   return hipGetLastError();
 }

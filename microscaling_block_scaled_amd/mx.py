@@ -48,6 +48,8 @@ def _load():
     lib.mx_dequantize.argtypes = [P, P, i32, i64, i64, P, P]
     lib.mx_gemm.restype = ctypes.c_int
     lib.mx_gemm.argtypes = [P, P, i32, P, P, i32, i64, i64, i64, P, i64, P]
+    lib.mx_gemm_mx.restype = ctypes.c_int
+    lib.mx_gemm_mx.argtypes = [P, P, i32, P, P, i32, i64, i64, i64, i32, P, P, P]
     lib.mx_packed_bytes.restype = i64
     lib.mx_packed_bytes.argtypes = [i32, i64, i64]
     lib.mx_scale_bytes.restype = i64
@@ -62,8 +64,8 @@ def _load():
 lib = _load()
 
 # every symbol include/mx.h declares
-EXPORTS = ("mx_quantize", "mx_dequantize", "mx_gemm", "mx_packed_bytes", "mx_scale_bytes",
-           "mx_status_str", "mx_version")
+EXPORTS = ("mx_quantize", "mx_dequantize", "mx_gemm", "mx_gemm_mx", "mx_packed_bytes",
+           "mx_scale_bytes", "mx_status_str", "mx_version")
 
 
 def status_str(status: int) -> str:
@@ -146,3 +148,21 @@ def gemm(a_q: torch.Tensor, a_s: torch.Tensor, a_fmt: int, b_q: torch.Tensor, b_
     _check(lib.mx_gemm(_ptr(a_q), _ptr(a_s), a_fmt, _ptr(b_q), _ptr(b_s), b_fmt, M, N, K,
                        _ptr(c), c.stride(0), _stream(stream)), "mx_gemm")
     return c
+
+
+def gemm_mx(a_q: torch.Tensor, a_s: torch.Tensor, a_fmt: int, b_q: torch.Tensor,
+            b_s: torch.Tensor, b_fmt: int, M: int, N: int, K: int, c_fmt: int,
+            out: dict | None = None, stream=None) -> dict:
+    """The product of ``gemm`` quantized row-wise (blocks of 32 along N, round to
+    nearest even) into format ``c_fmt`` inside the GEMM.  Returns uint8 device
+    tensors q_row [M, N * bits / 8] and s_row [M, N / 32]; ``out`` may supply
+    them preallocated."""
+    o = dict(out or {})
+    dev = a_q.device
+    if "q_row" not in o:
+        o["q_row"] = torch.empty((M, N * BITS[c_fmt] // 8), dtype=torch.uint8, device=dev)
+        o["s_row"] = torch.empty((M, N // 32), dtype=torch.uint8, device=dev)
+    _check(lib.mx_gemm_mx(_ptr(a_q), _ptr(a_s), a_fmt, _ptr(b_q), _ptr(b_s), b_fmt, M, N, K,
+                          c_fmt, _ptr(o["q_row"]), _ptr(o["s_row"]), _stream(stream)),
+           "mx_gemm_mx")
+    return o

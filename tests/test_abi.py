@@ -114,3 +114,30 @@ def test_gemm_validation(mx):
     assert g(a=None) == mx.MX_ERR_ARG
     assert g(a=FAKE + 2) == mx.MX_ERR_ALIGN
     assert g(M=0, c=None) == mx.MX_OK
+
+
+@no_gpu
+def test_gemm_mx_validation(mx):
+    L = mx.lib
+    g = lambda af=0, bf=0, M=64, N=64, K=512, cf=0, a=FAKE, ascale=FAKE, cq=FAKE, cs=FAKE: \
+        L.mx_gemm_mx(a, ascale, af, FAKE, FAKE, bf, M, N, K, cf, cq, cs, None)
+    assert g(af=6) == mx.MX_ERR_ARG
+    assert g(cf=6) == mx.MX_ERR_ARG
+    assert g(cf=-1) == mx.MX_ERR_ARG
+    assert g(af=5) == mx.MX_ERR_UNSUPPORTED
+    for cf in (2, 3, 5):  # FP6 and INT8 outputs are not fused
+        assert g(cf=cf) == mx.MX_ERR_UNSUPPORTED
+    assert g(M=-1) == mx.MX_ERR_ARG
+    assert g(K=48) == mx.MX_ERR_SHAPE
+    assert g(N=48) == mx.MX_ERR_SHAPE
+    assert g(cq=None) == mx.MX_ERR_ARG
+    assert g(cs=None) == mx.MX_ERR_ARG
+    assert g(a=None) == mx.MX_ERR_ARG
+    assert g(cq=FAKE + 4) == mx.MX_ERR_ALIGN
+    assert g(a=FAKE + 2) == mx.MX_ERR_ALIGN
+    # outside the staged kernel: refused before any launch
+    assert g(K=96) == mx.MX_ERR_UNSUPPORTED
+    assert g(K=0) == mx.MX_ERR_UNSUPPORTED
+    assert g(ascale=FAKE + 1) == mx.MX_ERR_UNSUPPORTED
+    assert g(M=0, cq=None, cs=None) == mx.MX_OK
+    assert g(N=0, cq=None, cs=None) == mx.MX_OK

@@ -1,0 +1,184 @@
+"""GPU GEMM with the MX-format epilogue (mx_gemm_mx) through the C-ABI.
+
+The fused product is checked two ways:
+  * against the oracle: the fp64 product of the oracle's own operands (bit-equal
+    to the GPU's) bounds the GPU's fp32 product within the GEMM tolerance; every
+    output block's scale must then lie between the scales of the block maxima at
+    the two ends of that interval, and every element's value between the
+    round-down of the interval's low end and the round-up of its high end on the
+    format's grid (round to nearest even is monotone, saturation clamps);
+  * bit for bit against the two-kernel route it replaces: mx_gemm's fp32 C
+    quantized by mx_quantize (row layout, RNE) -- the same fp32 sums go into the
+    same block quantization, so the codes and scales must be identical."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import dev, gemm_tolerance, host, mfma_group_bound, say
+from test_gpu_gemm import FMT_NAMES, quant_pair
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mx():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    from microscaling_block_scaled_amd import mx as m
+    return m
+
+
+def grid(oracle, fmt):
+    """Every finite value of the element format, signed, sorted."""
+    v = [oracle.elem_value(fmt, c) for c in range(1 << oracle.elem_bits(fmt))]
+    return np.unique(np.array([x for x in v if np.isfinite(x)], np.float64))
+
+
+def scale_code_of(oracle, fmt, amax):
+    """E8M0 code of floor(log2 amax) - emax (0 for a block max below the fp32
+    normal range, which the flush makes a zero block)."""
+    m, e = np.frexp(amax)          # amax = m * 2^e, m in [0.5, 1)
+    code = (e - 1) + 127 - oracle.elem_emax(fmt)
+    return np.where(amax < 2.0 ** -126, 0, np.maximum(code, 0))
+
+
+def check_against_oracle(oracle, fmt, q, s, cref, tol, what):
+    """q/s: the GPU's row-wise MX output for rows of C whose fp64 values are
+    cref (same shape, blocks of 32 along the last axis) with bound tol."""
+    R, N = cref.shape
+    nb = N // 32
+    lo_abs = np.maximum(np.abs(cref) - tol, 0.0).reshape(R, nb, 32).max(axis=2)
+    hi_abs = (np.abs(cref) + tol).reshape(R, nb, 32).max(axis=2)
+    s = s.astype(np.int64)
+    s_lo, s_hi = scale_code_of(oracle, fmt, lo_abs), scale_code_of(oracle, fmt, hi_abs)
+    bad = (s < s_lo) | (s > s_hi)
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {bad.sum()} scales outside [{s_lo[i]}, {s_hi[i]}] "
+                             f"first at {i}: gpu {s[i]}")
+    X = np.exp2(np.repeat(s - 127, 32, axis=1).astype(np.float64))
+    y = oracle.dequantize(q, s.astype(np.uint8), fmt, R, N).astype(np.float64) / X
+    g = grid(oracle, fmt)
+    mn = oracle.elem_maxnorm(fmt)
+    y_lo = np.clip((cref - tol) / X, -mn, mn)
+    y_hi = np.clip((cref + tol) / X, -mn, mn)
+    down = g[np.searchsorted(g, y_lo, side="right") - 1]
+    up = g[np.minimum(np.searchsorted(g, y_hi, side="left"), len(g) - 1)]
+    bad = (y < down) | (y > up)
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} elements outside their "
+                             f"rounding interval; first at {i}: gpu {y[i]} allowed "
+                             f"[{down[i]}, {up[i]}] (C {cref[i]} +- {tol[i]}, X {X[i]})")
+
+
+def same_as_two_kernels(mx, ga, fa, gw, fw, M, N, K, fc, got, what):
+    c = mx.gemm(ga["q_row"], ga["s_row"], fa, gw["q_row"], gw["s_row"], fw, M, N, K)
+    r = mx.quantize(c, fc, 1, 0)
+    for k in ("q_row", "s_row"):
+        if not torch.equal(got[k], r[k]):
+            bad = (got[k] != r[k]).nonzero()
+            i = tuple(bad[0].tolist())
+            raise AssertionError(f"{what} {k}: {len(bad)} bytes differ from gemm + quantize, "
+                                 f"first at {i}: fused {int(got[k][i]):#x} "
+                                 f"two-kernel {int(r[k][i]):#x}")
+
+
+CASES = [(0, 0, 0), (1, 0, 1), (0, 0, 4), (4, 4, 4), (2, 4, 0), (4, 4, 0), (3, 1, 1)]
+
+
+@pytest.mark.parametrize("fa,fw,fc", CASES)
+def test_mx_output_small(mx, oracle, fa, fw, fc):
+    """Ragged M (not a multiple of the 256-row tile), N a multiple of 32 but not
+    of the 256-column tile, rows of A scaled over 2^-12 .. 2^12 so that block
+    scales spread, and one zero row of A (zero blocks: scale 0, codes 0)."""
+    rng = np.random.default_rng(100 + 10 * fa + fw + 1000 * fc)
+    from microscaling_block_scaled_amd.synth import bf16_bits
+    for (M, N, K) in [(288, 320, 1536), (100, 96, 512), (33, 32, 1024)]:
+        a = rng.standard_normal((M, K)) * np.exp2(rng.integers(-12, 13, (M, 1)))
+        a[M // 2] = 0.0
+        a = bf16_bits(a.astype(np.float32))
+        w = bf16_bits((rng.standard_normal((N, K)) * 0.05).astype(np.float32))
+        (ga, oa), (gw, ow) = quant_pair(mx, oracle, a, w, fa, fw)
+        what = f"{FMT_NAMES[fa]}x{FMT_NAMES[fw]}->{FMT_NAMES[fc]} {M}x{N}x{K}"
+        say("gemm_mx", what)
+        got = mx.gemm_mx(ga["q_row"], ga["s_row"], fa, gw["q_row"], gw["s_row"], fw, M, N, K, fc)
+        torch.cuda.synchronize()
+        cref, t = oracle.gemm_f64(oa["q_row"], oa["s_row"], fa, ow["q_row"], ow["s_row"], fw,
+                                  M, N, K)
+        extra = mfma_group_bound(oracle.dequantize(oa["q_row"], oa["s_row"], fa, M, K).astype(np.float64),
+                                 oracle.dequantize(ow["q_row"], ow["s_row"], fw, N, K).astype(np.float64))
+        check_against_oracle(oracle, fc, host(got["q_row"]), host(got["s_row"]), cref,
+                             gemm_tolerance(t) + extra, what)
+        assert (host(got["s_row"])[M // 2] == 0).all() and (host(got["q_row"])[M // 2] == 0).all()
+        say("gemm + quantize", what)
+        same_as_two_kernels(mx, ga, fa, gw, fw, M, N, K, fc, got, what)
+
+
+def test_mx_output_unsupported_and_empty(mx, oracle):
+    """Shapes outside the fused kernel are refused without writing; empty
+    products write nothing."""
+    rng = np.random.default_rng(5)
+    from microscaling_block_scaled_amd.synth import bf16_bits
+    M, N, K = 64, 64, 96
+    a = bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = bf16_bits(rng.standard_normal((N, K)).astype(np.float32))
+    (ga, _), (gw, _) = quant_pair(mx, oracle, a, w, 0, 0)
+    q = torch.full((M, N), 0x5A, dtype=torch.uint8, device="cuda")
+    s = torch.full((M, N // 32), 0x5A, dtype=torch.uint8, device="cuda")
+    say("gemm_mx K=96 (refused)")
+    with pytest.raises(mx.MXError) as e:
+        mx.gemm_mx(ga["q_row"], ga["s_row"], 0, gw["q_row"], gw["s_row"], 0, M, N, K, 0,
+                   out={"q_row": q, "s_row": s})
+    assert e.value.status == mx.MX_ERR_UNSUPPORTED
+    with pytest.raises(mx.MXError) as e:
+        mx.gemm_mx(ga["q_row"], ga["s_row"], 0, gw["q_row"], gw["s_row"], 0, M, N, K, 2,
+                   out={"q_row": q, "s_row": s})
+    assert e.value.status == mx.MX_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert (host(q) == 0x5A).all() and (host(s) == 0x5A).all()
+    say("gemm_mx M=0")
+    mx.gemm_mx(ga["q_row"], ga["s_row"], 0, gw["q_row"], gw["s_row"], 0, 0, N, 512, 0,
+               out={"q_row": q[:0], "s_row": s[:0]})
+
+
+@pytest.mark.parametrize("cfg,fc", [("mxfp8_mlp", 0), ("mxfp4_mlp", 4)])
+def test_mx_output_full_size(mx, oracle, cfg, fc):
+    """The Llama-3-8B MLP shape at full size in the launch the benchmark times:
+    bit-identical to gemm + quantize over the whole output, and within the
+    oracle's bounds on 96 sampled output blocks (plus the four corner blocks)."""
+    from microscaling_block_scaled_amd.synth import make
+    d = make(cfg)
+    a, w = d["A"], d["W"]
+    if cfg == "mxfp8_mlp":
+        fa, fw, akw, wkw = 0, 0, {}, {}
+    else:
+        fa, fw, akw, wkw = 4, 4, {"round": 1, "had": True, "seed": 42}, {"had": True}
+    (ga, oa), (gw, ow) = quant_pair(mx, oracle, a, w, fa, fw, akw, wkw)
+    M, K = a.shape
+    N = w.shape[0]
+    what = f"{cfg}->{FMT_NAMES[fc]} {M}x{N}x{K}"
+    say("gemm_mx", what)
+    got = mx.gemm_mx(ga["q_row"], ga["s_row"], fa, gw["q_row"], gw["s_row"], fw, M, N, K, fc)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    nb = N // 32
+    rows = np.concatenate([rng.integers(0, M, 96), [0, 0, M - 1, M - 1]])
+    blks = np.concatenate([rng.integers(0, nb, 96), [0, nb - 1, 0, nb - 1]])
+    ms = np.repeat(rows, 32)
+    ns = (blks[:, None] * 32 + np.arange(32)[None, :]).reshape(-1)
+    cref, t = oracle.gemm_f64_at(oa["q_row"], oa["s_row"], fa, ow["q_row"], ow["s_row"], fw,
+                                 M, N, K, ms, ns)
+    S = len(ms)
+    ad = oracle.dequantize(np.ascontiguousarray(oa["q_row"][ms]), np.ascontiguousarray(oa["s_row"][ms]),
+                           fa, S, K).astype(np.float64)
+    wd = oracle.dequantize(np.ascontiguousarray(ow["q_row"][ns]), np.ascontiguousarray(ow["s_row"][ns]),
+                           fw, S, K).astype(np.float64)
+    tol = gemm_tolerance(t) + mfma_group_bound(ad, wd, pairs=(np.arange(S), np.arange(S)))
+    # the sampled blocks' codes and scales, as one [samples x 32] output
+    qh, sh = host(got["q_row"]), host(got["s_row"])
+    bpb = 32 * oracle.elem_bits(fc) // 8  # bytes per block
+    qs = np.stack([qh[r, b * bpb:(b + 1) * bpb] for r, b in zip(rows, blks)])
+    ss = np.array([[sh[r, b]] for r, b in zip(rows, blks)], np.uint8)
+    check_against_oracle(oracle, fc, qs, ss, cref.reshape(-1, 32), tol.reshape(-1, 32), what)
+    say("gemm + quantize", what)
+    same_as_two_kernels(mx, ga, fa, gw, fw, M, N, K, fc, got, what)
