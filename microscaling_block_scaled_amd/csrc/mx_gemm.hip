@@ -435,6 +435,21 @@ __device__ __forceinline__ void substep(v16f (&acc)[4][4], const Ops& cur, Slot&
   });
 }
 
+// Element k of an accumulator tile as fp32 bits, read from its accumulation
+// register at this point of the program.  Left to itself the compiler copies
+// every accumulator of the epilogue into vector registers at its start, which
+// for 256 values spills; a read in the asm keeps each value in place until it
+// is used.  The compiler does not count wait states for asm, so the first
+// such read must follow acc_settle: a read of an accumulator needs 18 wait
+// states after the 16-pass matrix instruction that wrote it.  Both are
+// volatile, which keeps them in program order.
+__device__ __forceinline__ uint32_t acc_bits(const v16f& t, int k) {
+  uint32_t r;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(t[k]));
+  return r;
+}
+__device__ __forceinline__ void acc_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory"); }
+
 // MX output of the product: C row-wise in MX format, blocks of 32 along N
 // (Algorithm 1 of the MX summary, section 3, applied to each fp32 block of the
 // product, round to nearest even), as "Format-Aware Fusion for Fast FP4
@@ -445,11 +460,16 @@ struct MxOut {
   uint8_t* s;      // [M x N/32] scales
 };
 
-// A wave's 128 x 128 piece (rows r0.., columns c0.., c0 % 32 == 0) as MX
+// A wave's 128 x 128 piece (rows r0.., columns c0.., c0 % 128 == 0) as MX
 // blocks: the 32 columns of acc[i][j] for row 32 i + l % 32 are one block,
-// held half by lane l (columns 8 q + e) and half by lane l ^ 32 (8 q + 4 + e).
-// The block max and the codes' halves are exchanged between the two lanes, so
-// each lane stores 16 consecutive columns' codes in one piece.
+// held half by lane l (columns 8 q + 4 (l / 32) + e, q and e in 0..3) and half
+// by lane l ^ 32.  The block max and the codes' halves are exchanged between
+// the two lanes, so each lane stores 16 consecutive columns' codes in one
+// piece.  Each step runs over the four tiles of a tile row at once, without
+// per-tile branches, so the exchanges of different tiles overlap: the
+// hardware conversion is applied to every block and replaced afterwards, on
+// the rare lanes that need it, by the exact conversion (scale codes below
+// DazFree) or the NaN codes.
 template <int F>
 __device__ __forceinline__ void store_mx(const v16f (&acc)[4][4], const MxOut& mo, int64_t r0, int64_t c0,
                                          int64_t M, int64_t N, int lane) {
@@ -457,47 +477,87 @@ __device__ __forceinline__ void store_mx(const v16f (&acc)[4][4], const MxOut& m
   const int lr = lane & 31, hi = lane >> 5;
   const int partner = (lane ^ 32) << 2;
   const int64_t nb = N >> 5;
+  const int64_t blk0 = c0 >> 5;
+  const bool s_dword = (nb & 3) == 0 && ((uintptr_t)mo.s & 3) == 0 && blk0 + 3 < nb;
+  acc_settle();
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int64_t row = r0 + 32 * i + lr;
+    // the element values of tile (i, j) as fp32 bits, read from the
+    // accumulation registers where they are used (acc_bits)
+    auto vals = [&](int j, int k0, uint32_t (&v)[8]) {
+#pragma unroll
+      for (int k = 0; k < 8; k++) v[k] = acc_bits(acc[i][j], k0 + k);
+    };
+    uint32_t code[4];
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      const v16f& t = acc[i][j];
-      uint32_t v[16];
       uint32_t am = 0;
 #pragma unroll
-      for (int k = 0; k < 16; k++) {
-        // the element is read into a scalar first: a bit cast applied
-        // directly to a vector-element expression reads element 0
-        const float e = t[k];
-        v[k] = __builtin_bit_cast(uint32_t, e);
-        am = umax(am, v[k] & 0x7FFFFFFFu);
-      }
-      am = umax(am, (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)am));
-      const uint32_t code = scale_code<F>(am);
+      for (int k = 0; k < 16; k++) am = umax(am, acc_bits(acc[i][j], k) & 0x7FFFFFFFu);
+      code[j] = am;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+      code[j] = scale_code<F>(umax(code[j], (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)code[j])));
+    Pack8 p[4][2];
+    bool slow = false;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      uint32_t v[8];
+      vals(j, 0, v);
+      p[j][0] = hw_convert8<F>(v, code[j]);
+      vals(j, 8, v);
+      p[j][1] = hw_convert8<F>(v, code[j]);
+      slow |= !hw_ok<F>(code[j]);
+    }
+    if (slow) {
       uint32_t rnd[8];
-      // codes of this lane's columns: groups q = 0..3 of four, at 8 q + 4 hi
-      const Pack8 p0 = convert8<F, false>(&v[0], code, rnd);  // groups 0, 1
-      const Pack8 p1 = convert8<F, false>(&v[8], code, rnd);  // groups 2, 3
-      const int64_t blk = (c0 >> 5) + j;
-      const bool live = row < M && blk < nb;
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        if (!hw_ok<F>(code[j])) {
+          uint32_t v[8];
+          vals(j, 0, v);
+          p[j][0] = convert8<F, false>(v, code[j], rnd);
+          vals(j, 8, v);
+          p[j][1] = convert8<F, false>(v, code[j], rnd);
+        }
+    }
+    // codes of this lane's columns: groups q = 0..3 of four, at 8 q + 4 hi;
+    // p[j][0] holds groups 0, 1 and p[j][1] groups 2, 3.  The values to send
+    // are fixed in registers before the exchanges, so the per-lane choice
+    // cannot become branches around them.
+    uint32_t x[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
       if (bits == 8) {
-        // group dwords g[q]; the low lane keeps groups 0-1 of both lanes
-        // (columns 0-15), the high lane groups 2-3 (columns 16-31)
-        const uint32_t g0 = p0.w[0], g1 = p0.w[1], g2 = p1.w[0], g3 = p1.w[1];
-        // the values to send are fixed in registers before the exchanges, so
-        // the per-lane choice cannot become branches around them
-        uint32_t s1 = hi ? g0 : g2, s2 = hi ? g1 : g3;
+        // the low lane keeps groups 0-1 of both lanes (columns 0-15), the
+        // high lane groups 2-3 (columns 16-31)
+        uint32_t s1 = hi ? p[j][0].w[0] : p[j][1].w[0];
+        uint32_t s2 = hi ? p[j][0].w[1] : p[j][1].w[1];
         asm volatile("" : "+v"(s1), "+v"(s2));
-        const uint32_t r1 = (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)s1);
-        const uint32_t r2 = (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)s2);
+        x[j][0] = (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)s1);
+        x[j][1] = (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)s2);
+      } else {  // E2M1: group q is 16 bits (w[0]: groups 0 | 1 << 16 or 2 | 3 << 16)
+        uint32_t s1 = hi ? p[j][0].w[0] : p[j][1].w[0];
+        asm volatile("" : "+v"(s1));
+        x[j][0] = (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)s1);
+      }
+    }
+    const bool rlive = row < M;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int64_t blk = blk0 + j;
+      const bool live = rlive && blk < nb;
+      if (bits == 8) {
+        const uint32_t g0 = p[j][0].w[0], g1 = p[j][0].w[1];
+        const uint32_t g2 = p[j][1].w[0], g3 = p[j][1].w[1];
+        const uint32_t r1 = x[j][0], r2 = x[j][1];
         const uint4 o = hi ? make_uint4(r1, g2, r2, g3) : make_uint4(g0, r1, g1, r2);
         if (live) *(uint4*)(mo.q + row * N + 32 * blk + 16 * hi) = o;
-      } else {  // E2M1: group q is 16 bits (p0: groups 0 | 1 << 16, p1: 2 | 3 << 16)
-        uint32_t s1 = hi ? p0.w[0] : p1.w[0];
-        asm volatile("" : "+v"(s1));
-        const uint32_t r = (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)s1);
-        const uint32_t own = hi ? p1.w[0] : p0.w[0];
+      } else {
+        const uint32_t r = x[j][0];
+        const uint32_t own = hi ? p[j][1].w[0] : p[j][0].w[0];
         uint2 o;
         if (hi) {  // columns 16-31: groups 2 (partner, own), 3 (partner, own)
           o.x = (r & 0xFFFFu) | (own << 16);
@@ -508,7 +568,18 @@ __device__ __forceinline__ void store_mx(const v16f (&acc)[4][4], const MxOut& m
         }
         if (live) *(uint2*)(mo.q + row * (N >> 1) + 16 * blk + 8 * hi) = o;
       }
-      if (live && hi == 0) mo.s[row * nb + blk] = (uint8_t)code;
+    }
+    // scales: both lanes of a row hold its four codes; the low lane stores
+    // them, as one dword where the row's scale offset is 4-byte aligned
+    if (rlive && hi == 0) {
+      uint8_t* sp = mo.s + row * nb + blk0;
+      if (s_dword) {
+        *(uint32_t*)sp = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          if (blk0 + j < nb) sp[j] = (uint8_t)code[j];
+      }
     }
   }
 }
