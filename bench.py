@@ -149,6 +149,37 @@ def bench_gemm(mx, name, a_host, w_host, fa, fw, peak, rounds=20, out_fmt=None):
             "frac_peak": round(tf / peak, 4), "peak_TFLOP/s": peak}
 
 
+def bench_linear(mx, fmt, peak, rounds=10):
+    """One training step of an MX linear layer at the Llama-3-8B MLP
+    up-projection shape (X [8192x4096], W [14336x4096], dY [8192x14336], bf16):
+    forward, dgrad and wgrad with every quantization the recipe calls for."""
+    import torch
+    from microscaling_block_scaled_amd import linear
+    from microscaling_block_scaled_amd.synth import make
+    d = make("mxfp8_mlp")
+    x, w = dev_bf16(d["A"]), dev_bf16(d["W"])
+    del d
+    T, H = x.shape
+    O = w.shape[0]
+    g = torch.Generator(device="cuda").manual_seed(5)
+    dy = (torch.randn((T, O), generator=g, device="cuda") * 1e-3).to(torch.bfloat16)
+    r = linear.Recipe(fmt=fmt, seed=42)
+
+    def run(i):
+        y, saved = linear.forward(x, w, r)
+        linear.backward(dy, saved, r)
+    for i in range(3):
+        run(i)
+    med, _ = timed_events(run, max(rounds // 5, 2), torch.cuda.current_stream())
+    tf = 3 * 2.0 * T * H * O / (med * 1e-3) / 1e12
+    del x, w, dy
+    torch.cuda.empty_cache()
+    return {"workload": f"MX linear fwd+dgrad+wgrad T={T} H={H} O={O}, {mx.FMT_NAMES[fmt]}, "
+                        "bf16 in, bf16 Y/dX, fp32 dW, SR on dY, H32 on wgrad operands",
+            "ms": round(med, 5), "TFLOP/s": round(tf, 1), "frac_peak": round(tf / peak, 4),
+            "peak_TFLOP/s": peak}
+
+
 def cpu_baseline():
     """The CPU oracle, timed on a bounded sample of the same step and scaled to
     the full step: quantize 1024 rows of A (H32 + SR), 384 rows of W (H32 + RNE),
@@ -287,6 +318,8 @@ def main():
         ks["gemm_mxfp6x4_mlp"] = bench_gemm(mx, "E2M3 activations x E2M1 weights M=8192 N=4096 K=14336",
                                             d["A"], d["W"], mx.E2M3, mx.E2M1, PEAK_TFLOPS["fp6"])
         del d
+        ks["linear_step_mxfp4"] = bench_linear(mx, mx.E2M1, PEAK_TFLOPS["fp4"])
+        ks["linear_step_mxfp8"] = bench_linear(mx, mx.E4M3, PEAK_TFLOPS["fp8"])
         out["kernels"] = ks
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()

@@ -143,6 +143,18 @@ int mx_gemm(const void* a_q, const uint8_t* a_s, int32_t a_fmt, const void* b_q,
             int64_t ldc, mx_stream_t stream);
 
 /*
+ * mx_gemm_bf16 -- the product of mx_gemm, each fp32 element rounded to bf16
+ * (nearest even; NaN stays NaN, fp32 subnormals give bf16 subnormals) as it
+ * leaves the kernel: the 16-bit output a linear layer hands to the next one.
+ * Arguments as for mx_gemm except
+ *   c  [M x N] bf16 bit patterns, leading dimension ldc >= N elements,
+ *      2-byte aligned (16-byte aligned with ldc % 4 == 0 stores 8 bytes at a time).
+ */
+int mx_gemm_bf16(const void* a_q, const uint8_t* a_s, int32_t a_fmt, const void* b_q,
+                 const uint8_t* b_s, int32_t b_fmt, int64_t M, int64_t N, int64_t K, uint16_t* c,
+                 int64_t ldc, mx_stream_t stream);
+
+/*
  * mx_gemm_mx -- the product of mx_gemm written straight out in MX format:
  * each fp32 row block C[m, 32 j .. 32 j + 31] is quantized as Algorithm 1 of
  * the MX summary (section 3) does it -- shared scale from the block max,

@@ -113,6 +113,23 @@ int mx_gemm(const void* a_q, const uint8_t* a_s, int32_t a_fmt, const void* b_q,
                                     nullptr, (hipStream_t)stream));
 }
 
+int mx_gemm_bf16(const void* a_q, const uint8_t* a_s, int32_t a_fmt, const void* b_q,
+                 const uint8_t* b_s, int32_t b_fmt, int64_t M, int64_t N, int64_t K, uint16_t* c,
+                 int64_t ldc, mx_stream_t stream) {
+  if (!fmt_ok(a_fmt) || !fmt_ok(b_fmt)) return MX_ERR_ARG;
+  if (a_fmt == MX_INT8 || b_fmt == MX_INT8) return MX_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || K < 0) return MX_ERR_ARG;
+  if (K % 32) return MX_ERR_SHAPE;
+  if (ldc < N) return MX_ERR_SHAPE;
+  if (M == 0 || N == 0) return MX_OK;
+  if (!c) return MX_ERR_ARG;
+  if (K > 0 && (!a_q || !a_s || !b_q || !b_s)) return MX_ERR_ARG;
+  if (K > 0 && (!aligned16(a_q) || !aligned16(b_q))) return MX_ERR_ALIGN;
+  if ((uintptr_t)c % 2) return MX_ERR_ALIGN;
+  return hip_status(mx::launch_gemm(a_q, a_s, a_fmt, b_q, b_s, b_fmt, M, N, K, nullptr, ldc,
+                                    mx::GEMM_OUT_BF16, (uint8_t*)c, nullptr, (hipStream_t)stream));
+}
+
 int mx_gemm_mx(const void* a_q, const uint8_t* a_s, int32_t a_fmt, const void* b_q,
                const uint8_t* b_s, int32_t b_fmt, int64_t M, int64_t N, int64_t K,
                int32_t c_fmt, void* c_q, uint8_t* c_s, mx_stream_t stream) {

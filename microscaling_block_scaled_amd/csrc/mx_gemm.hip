@@ -139,13 +139,24 @@ __device__ __forceinline__ v8i read_operand(const uint8_t* panel, int row, int k
   return v;
 }
 
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN), by the
+// hardware conversion; fp32 subnormals are kept.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+__device__ __forceinline__ uint16_t bf16_bits(float a) {
+  return __builtin_bit_cast(uint16_t, (__bf16)a);
+}
+
 template <int FA, int FB>
 __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ aq,
                                               const uint8_t* __restrict__ as,
                                               const uint8_t* __restrict__ bq,
                                               const uint8_t* __restrict__ bs, int64_t M,
                                               int64_t N, int64_t K, float* __restrict__ c,
-                                              int64_t ldc, int tiles_n) {
+                                              uint16_t* __restrict__ cb, int64_t ldc, int tiles_n) {
   using L = GemmLds<FA, FB>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -212,7 +223,12 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ aq,
 #pragma unroll
       for (int v = 0; v < 4; v++) {
         const int64_t row = m0 + wm * 128 + i * 16 + 4 * kb + v;
-        if (row < M && col < N) c[row * ldc + col] = acc[i][j][v];
+        if (row < M && col < N) {
+          if (cb)
+            cb[row * ldc + col] = bf16_bits(acc[i][j][v]);
+          else
+            c[row * ldc + col] = acc[i][j][v];
+        }
       }
     }
   }
@@ -455,7 +471,7 @@ __device__ __forceinline__ void acc_settle() { asm volatile("s_nop 7\n\ts_nop 7\
 // product, round to nearest even), as "Format-Aware Fusion for Fast FP4
 // Pretraining" fuses the quantization into the producer.
 struct MxOut {
-  int fmt;         // E4M3, E5M2 or E2M1; negative: fp32 C
+  int fmt;         // E4M3, E5M2 or E2M1; GEMM_OUT_BF16: bf16 C at q; negative: fp32 C
   uint8_t* q;      // [M x N] packed codes, row pitch N * bits / 8
   uint8_t* s;      // [M x N/32] scales
 };
@@ -763,6 +779,33 @@ __global__ __launch_bounds__(256) void k_gemm_fast(const uint8_t* __restrict__ a
 
   // acc[i][j] is the 32 x 32 tile C^T[n][m]: lane l holds, for v = 4q + e,
   // C[m0 + wm*128 + 32 i + l % 32][n0 + wn*128 + 32 j + 8 q + 4 (l / 32) + e]
+  if (mo.fmt == GEMM_OUT_BF16) {  // bf16 C, row pitch ldc elements
+    uint16_t* cb = (uint16_t*)mo.q;
+    const int lr = lane & 31;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int64_t row = m0 + wm * 128 + i * 32 + lr;
+      if (row >= M) continue;
+      uint16_t* crow = cb + row * ldc;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int64_t col = n0 + wn * 128 + j * 32 + 8 * q + 4 * w.kb;
+          const v16f& tt = acc[i][j];
+          if (vec_store && col + 3 < N) {
+            *(uint2*)(crow + col) = make_uint2(bf16x2_bits(tt[4 * q], tt[4 * q + 1]),
+                                               bf16x2_bits(tt[4 * q + 2], tt[4 * q + 3]));
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+              if (col + e < N) crow[col + e] = bf16_bits(tt[4 * q + e]);
+          }
+        }
+      }
+    }
+    return;
+  }
   if (mo.fmt >= 0) {  // wave-uniform: MX output
     switch (mo.fmt) {
       case E4M3: store_mx<E4M3>(acc, mo, m0 + wm * 128, n0 + wn * 128, M, N, lane); break;
@@ -799,7 +842,8 @@ template <int FA, int FB, int KS>
 static hipError_t launch_fast(const void* aq, const uint8_t* as, const void* bq, const uint8_t* bs,
                               int64_t M, int64_t N, int64_t K, float* c, int64_t ldc,
                               int64_t tiles_m, int64_t tiles_n, const MxOut& mo, hipStream_t st) {
-  const int vec = ((uintptr_t)c % 16) == 0 && ldc % 4 == 0;
+  const int vec = mo.fmt == GEMM_OUT_BF16 ? ((uintptr_t)mo.q % 8) == 0 && ldc % 4 == 0
+                                            : ((uintptr_t)c % 16) == 0 && ldc % 4 == 0;
   hipLaunchKernelGGL((k_gemm_fast<FA, FB, KS>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
                      st, (const uint8_t*)aq, as, (const uint8_t*)bq, bs, M, N, K, c, ldc,
                      (int)tiles_m, (int)tiles_n, vec, mo);
@@ -828,7 +872,7 @@ static hipError_t gemm_launch(const void* aq, const uint8_t* as, const void* bq,
     else
       return launch_fast<FA, FB, 128>(aq, as, bq, bs, M, N, K, c, ldc, tiles_m, tiles_n, mo, st);
   }
-  if (mo.fmt >= 0) return hipErrorNotSupported;  // MX output: the staged kernel only
+  if (mo.fmt >= 0 && mo.fmt != GEMM_OUT_BF16) return hipErrorNotSupported;  // MX output: staged only
   using L = GemmLds<FA, FB>;
   static bool attr_done = false;  // benign race: the call is idempotent
   if (!attr_done) {
@@ -838,8 +882,8 @@ static hipError_t gemm_launch(const void* aq, const uint8_t* as, const void* bq,
     attr_done = true;
   }
   hipLaunchKernelGGL((k_gemm<FA, FB>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), L::TOTAL, st,
-                     (const uint8_t*)aq, as, (const uint8_t*)bq, bs, M, N, K, c, ldc,
-                     (int)tiles_n);
+                     (const uint8_t*)aq, as, (const uint8_t*)bq, bs, M, N, K, c,
+                     mo.fmt == GEMM_OUT_BF16 ? (uint16_t*)mo.q : nullptr, ldc, (int)tiles_n);
   return hipGetLastError();
 }
 

@@ -26,9 +26,11 @@ hipError_t launch_quant_rows(const QuantArgs& a, hipStream_t st);
 hipError_t launch_quant_tiles(const QuantArgs& a, bool with_rows, hipStream_t st);
 hipError_t launch_dequant(const void* q, const uint8_t* s, int fmt, int64_t rows, int64_t cols,
                           float* y, hipStream_t st);
-// out_fmt < 0: fp32 C (c, ldc).  Otherwise C goes out row-wise in MX format
-// out_fmt (E4M3, E5M2, E2M1) to out_q / out_s; only the staged kernel does
-// that (hipErrorNotSupported otherwise).
+// out_fmt < 0: fp32 C (c, ldc).  GEMM_OUT_BF16: bf16 C at out_q, row pitch
+// ldc elements.  Otherwise C goes out row-wise in MX format out_fmt (E4M3,
+// E5M2, E2M1) to out_q / out_s; only the staged kernel does that
+// (hipErrorNotSupported otherwise).
+constexpr int GEMM_OUT_BF16 = 16;
 hipError_t launch_gemm(const void* a_q, const uint8_t* a_s, int a_fmt, const void* b_q,
                        const uint8_t* b_s, int b_fmt, int64_t M, int64_t N, int64_t K, float* c,
                        int64_t ldc, int out_fmt, uint8_t* out_q, uint8_t* out_s, hipStream_t st);

@@ -15,6 +15,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmx.so")
 
 E4M3, E5M2, E2M3, E3M2, E2M1, INT8 = range(6)
+FMT_NAMES = ("e4m3", "e5m2", "e2m3", "e3m2", "e2m1", "int8")
 FORMATS = {"e4m3": E4M3, "e5m2": E5M2, "e2m3": E2M3, "e3m2": E3M2, "e2m1": E2M1, "int8": INT8}
 BITS = {E4M3: 8, E5M2: 8, E2M3: 6, E3M2: 6, E2M1: 4, INT8: 8}
 SRC_F32, SRC_BF16 = 0, 1
@@ -48,6 +49,8 @@ def _load():
     lib.mx_dequantize.argtypes = [P, P, i32, i64, i64, P, P]
     lib.mx_gemm.restype = ctypes.c_int
     lib.mx_gemm.argtypes = [P, P, i32, P, P, i32, i64, i64, i64, P, i64, P]
+    lib.mx_gemm_bf16.restype = ctypes.c_int
+    lib.mx_gemm_bf16.argtypes = [P, P, i32, P, P, i32, i64, i64, i64, P, i64, P]
     lib.mx_gemm_mx.restype = ctypes.c_int
     lib.mx_gemm_mx.argtypes = [P, P, i32, P, P, i32, i64, i64, i64, i32, P, P, P]
     lib.mx_packed_bytes.restype = i64
@@ -64,8 +67,8 @@ def _load():
 lib = _load()
 
 # every symbol include/mx.h declares
-EXPORTS = ("mx_quantize", "mx_dequantize", "mx_gemm", "mx_gemm_mx", "mx_packed_bytes",
-           "mx_scale_bytes", "mx_status_str", "mx_version")
+EXPORTS = ("mx_quantize", "mx_dequantize", "mx_gemm", "mx_gemm_bf16", "mx_gemm_mx",
+           "mx_packed_bytes", "mx_scale_bytes", "mx_status_str", "mx_version")
 
 
 def status_str(status: int) -> str:
@@ -147,6 +150,19 @@ def gemm(a_q: torch.Tensor, a_s: torch.Tensor, a_fmt: int, b_q: torch.Tensor, b_
         c = torch.empty((M, N), dtype=torch.float32, device=a_q.device)
     _check(lib.mx_gemm(_ptr(a_q), _ptr(a_s), a_fmt, _ptr(b_q), _ptr(b_s), b_fmt, M, N, K,
                        _ptr(c), c.stride(0), _stream(stream)), "mx_gemm")
+    return c
+
+
+def gemm_bf16(a_q: torch.Tensor, a_s: torch.Tensor, a_fmt: int, b_q: torch.Tensor,
+              b_s: torch.Tensor, b_fmt: int, M: int, N: int, K: int,
+              c: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """``gemm`` with C rounded to bf16 (nearest even) in the kernel."""
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
+    if c.dtype != torch.bfloat16 or (c.dim() == 2 and c.shape[0] > 0 and c.stride(1) != 1):
+        raise ValueError("c must be a bf16 tensor with unit column stride")
+    _check(lib.mx_gemm_bf16(_ptr(a_q), _ptr(a_s), a_fmt, _ptr(b_q), _ptr(b_s), b_fmt, M, N, K,
+                            _ptr(c), c.stride(0), _stream(stream)), "mx_gemm_bf16")
     return c
 
 

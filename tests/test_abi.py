@@ -20,7 +20,7 @@ def mx():
 def header_functions():
     src = open(os.path.join(ROOT, "include", "mx.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(mx_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(mx_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol(mx):
@@ -141,3 +141,20 @@ def test_gemm_mx_validation(mx):
     assert g(ascale=FAKE + 1) == mx.MX_ERR_UNSUPPORTED
     assert g(M=0, cq=None, cs=None) == mx.MX_OK
     assert g(N=0, cq=None, cs=None) == mx.MX_OK
+
+
+@no_gpu
+def test_gemm_bf16_validation(mx):
+    L = mx.lib
+    g = lambda af=0, bf=0, M=64, N=64, K=64, ldc=64, a=FAKE, c=FAKE: L.mx_gemm_bf16(
+        a, FAKE, af, FAKE, FAKE, bf, M, N, K, c, ldc, None)
+    assert g(af=6) == mx.MX_ERR_ARG
+    assert g(af=5) == mx.MX_ERR_UNSUPPORTED
+    assert g(M=-1) == mx.MX_ERR_ARG
+    assert g(K=48) == mx.MX_ERR_SHAPE
+    assert g(ldc=63) == mx.MX_ERR_SHAPE
+    assert g(c=None) == mx.MX_ERR_ARG
+    assert g(a=None) == mx.MX_ERR_ARG
+    assert g(a=FAKE + 2) == mx.MX_ERR_ALIGN
+    assert g(c=FAKE + 1) == mx.MX_ERR_ALIGN
+    assert g(M=0, c=None) == mx.MX_OK
