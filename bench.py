@@ -25,7 +25,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MX quantize GB/s + MX-GEMM TFLOPS (MXFP8/MXFP4), % of HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0
-PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0, "fp6": 10100.0}
+PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0, "fp6": 10100.0, "bf16": 2500.0}
 M, N, K = 8192, 4096, 14336
 
 
@@ -308,6 +308,10 @@ def main():
             PEAK_TFLOPS["fp8"], out_fmt=mx.E4M3)
         del d
         d = make("mxfp8_grad")
+        # MXINT8 runs on the bf16 instruction with the scales folded into the
+        # operands: priced against the bf16 peak
+        ks["gemm_mxint8_mlp"] = bench_gemm(mx, "INT8 x INT8 M=8192 N=14336 K=4096 (bf16 MFMA)",
+                                           d["A"], d["W"], mx.INT8, mx.INT8, PEAK_TFLOPS["bf16"])
         ks["gemm_mxfp8_grad"] = bench_gemm(mx, "E5M2 x E4M3 M=4096 N=4096 K=14336", d["A"],
                                            d["W"], mx.E5M2, mx.E4M3, PEAK_TFLOPS["fp8"])
         del d

@@ -132,8 +132,11 @@ int mx_dequantize(const void* q, const uint8_t* s, int32_t fmt, int64_t rows, in
  *             mx_quantize produces for a weight W[N x K] row-wise, or for B[K x N]
  *             with MX_LAYOUT_COLT.
  *   c         [M x N] fp32, leading dimension ldc >= N.
- * Formats: E4M3, E5M2, E2M3, E3M2, E2M1 for either operand (any mix); MX_INT8
- * returns MX_ERR_UNSUPPORTED.  K % 32 == 0; operand pointers 16-byte aligned.
+ * Formats: E4M3, E5M2, E2M3, E3M2, E2M1 for either operand (any mix), or
+ * MX_INT8 for both (INT8 mixed with another format returns
+ * MX_ERR_UNSUPPORTED).  MXINT8 products are formed exactly (each element times
+ * its scale is exact in bf16 wherever it is a normal number) and summed in
+ * fp32.  K % 32 == 0; operand pointers 16-byte aligned.
  * The result of a block whose scale is 0xFF is unspecified (the hardware's
  * NaN-scale behaviour); no configuration here produces such scales from finite
  * inputs.

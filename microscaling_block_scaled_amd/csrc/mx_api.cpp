@@ -101,7 +101,7 @@ int mx_gemm(const void* a_q, const uint8_t* a_s, int32_t a_fmt, const void* b_q,
             const uint8_t* b_s, int32_t b_fmt, int64_t M, int64_t N, int64_t K, float* c,
             int64_t ldc, mx_stream_t stream) {
   if (!fmt_ok(a_fmt) || !fmt_ok(b_fmt)) return MX_ERR_ARG;
-  if (a_fmt == MX_INT8 || b_fmt == MX_INT8) return MX_ERR_UNSUPPORTED;
+  if ((a_fmt == MX_INT8) != (b_fmt == MX_INT8)) return MX_ERR_UNSUPPORTED;
   if (M < 0 || N < 0 || K < 0) return MX_ERR_ARG;
   if (K % 32) return MX_ERR_SHAPE;
   if (ldc < N) return MX_ERR_SHAPE;
@@ -117,7 +117,7 @@ int mx_gemm_bf16(const void* a_q, const uint8_t* a_s, int32_t a_fmt, const void*
                  const uint8_t* b_s, int32_t b_fmt, int64_t M, int64_t N, int64_t K, uint16_t* c,
                  int64_t ldc, mx_stream_t stream) {
   if (!fmt_ok(a_fmt) || !fmt_ok(b_fmt)) return MX_ERR_ARG;
-  if (a_fmt == MX_INT8 || b_fmt == MX_INT8) return MX_ERR_UNSUPPORTED;
+  if ((a_fmt == MX_INT8) != (b_fmt == MX_INT8)) return MX_ERR_UNSUPPORTED;
   if (M < 0 || N < 0 || K < 0) return MX_ERR_ARG;
   if (K % 32) return MX_ERR_SHAPE;
   if (ldc < N) return MX_ERR_SHAPE;

@@ -235,6 +235,147 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ aq,
 }
 
 // ---------------------------------------------------------------------------
+// MXINT8 x MXINT8
+// ---------------------------------------------------------------------------
+// gfx950's block-scaled matrix instruction takes no integer elements.  An
+// MXINT8 element n / 64 times its block scale 2^(s - 127) is n * 2^(s - 133):
+// an integer of at most 7 significant bits times a power of two, which bf16
+// holds exactly (8 significant bits) wherever the result is a normal number.
+// So each lane turns its operand bytes into bf16 with the scale folded in, and
+// a bf16 matrix instruction with K = 32 -- one block per instruction -- forms
+// the products exactly and accumulates them in fp32.  Folding the scale into
+// the operands costs one conversion per operand element per tile pass; an
+// integer instruction would instead need a per-output fp32 rescale after every
+// block, which the vector ALU cannot keep up with.  Values of blocks with scale
+// codes below 7 fall below bf16's normal range and round; their contribution
+// is below 2^-120 per product.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// 8 INT8 codes (w: bytes 0..7 = elements 0..7) of one block with scale code
+// s, as bf16 values n * 2^(s - 133).
+__device__ __forceinline__ v8bf i8_bf16(uint2 w, int s) {
+  const int e = s - 133;
+  float f[8];
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    f[k] = __builtin_amdgcn_ldexpf((float)(int)(int8_t)(w.x >> (8 * k)), e);
+    f[4 + k] = __builtin_amdgcn_ldexpf((float)(int)(int8_t)(w.y >> (8 * k)), e);
+  }
+  const uint4 p = make_uint4(bf16x2_bits(f[0], f[1]), bf16x2_bits(f[2], f[3]),
+                             bf16x2_bits(f[4], f[5]), bf16x2_bits(f[6], f[7]));
+  return __builtin_bit_cast(v8bf, p);
+}
+
+// Same tiling and staging as k_gemm (256 x 256 tile, four waves of 128 x 128,
+// K-steps of four blocks through two LDS stages); per block one 16x16x32 bf16
+// instruction per 16 x 16 output tile.  Lane l supplies row l % 16 of its
+// operand tile, elements 8 (l / 16) .. 8 (l / 16) + 7 of the block.
+__global__ __launch_bounds__(256) void k_gemm_i8(const uint8_t* __restrict__ aq,
+                                                 const uint8_t* __restrict__ as,
+                                                 const uint8_t* __restrict__ bq,
+                                                 const uint8_t* __restrict__ bs, int64_t M,
+                                                 int64_t N, int64_t K, float* __restrict__ c,
+                                                 uint16_t* __restrict__ cb, int64_t ldc,
+                                                 int tiles_n) {
+  using L = GemmLds<INT8, INT8>;
+  using O = Op<INT8>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+  const int64_t nblk = K / 32;
+  const int nk = (int)((K + KS - 1) / KS);
+  const int lr = lane & 15, kg = lane >> 4;
+
+  v4f acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; i++)
+#pragma unroll
+    for (int j = 0; j < 8; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  PanelRegs<INT8> ra, rb;
+  load_panel<INT8>(ra, aq, as, M, m0, K, nblk, 0, tid);
+  load_panel<INT8>(rb, bq, bs, N, n0, K, nblk, 0, tid);
+  store_panel<INT8>(ra, lds + L::A_OFF, lds + L::SA_OFF, tid);
+  store_panel<INT8>(rb, lds + L::B_OFF, lds + L::SB_OFF, tid);
+  __syncthreads();
+
+  for (int ks = 0; ks < nk; ks++) {
+    const int cur = ks & 1;
+    uint8_t* st = lds + cur * L::STAGE;
+    if (ks + 1 < nk) {
+      load_panel<INT8>(ra, aq, as, M, m0, K, nblk, (int64_t)(ks + 1) * KS, tid);
+      load_panel<INT8>(rb, bq, bs, N, n0, K, nblk, (int64_t)(ks + 1) * KS, tid);
+    }
+    // one block at a time keeps one block's converted operands live
+#pragma unroll 1
+    for (int b = 0; b < KS / 32; b++) {
+      v8bf bop[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const int row = wn * 128 + j * 16 + lr;
+        const uint2 w = *(const uint2*)(st + L::B_OFF + row * O::PITCH + 32 * b + 8 * kg);
+        bop[j] = i8_bf16(w, st[L::SB_OFF + row * 4 + b]);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const int row = wm * 128 + i * 16 + lr;
+        const uint2 w = *(const uint2*)(st + L::A_OFF + row * O::PITCH + 32 * b + 8 * kg);
+        const v8bf aop = i8_bf16(w, st[L::SA_OFF + row * 4 + b]);
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    if (ks + 1 < nk) {
+      uint8_t* nx = lds + (cur ^ 1) * L::STAGE;
+      store_panel<INT8>(ra, nx + L::A_OFF, nx + L::SA_OFF, tid);
+      store_panel<INT8>(rb, nx + L::B_OFF, nx + L::SB_OFF, tid);
+    }
+    __syncthreads();
+  }
+
+  // lane l holds C[4 (l / 16) + v][l % 16] of each 16 x 16 tile
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int64_t col = n0 + wn * 128 + j * 16 + lr;
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        const int64_t row = m0 + wm * 128 + i * 16 + 4 * kg + v;
+        if (row < M && col < N) {
+          if (cb)
+            cb[row * ldc + col] = bf16_bits(acc[i][j][v]);
+          else
+            c[row * ldc + col] = acc[i][j][v];
+        }
+      }
+    }
+  }
+}
+
+static hipError_t gemm_i8_launch(const void* aq, const uint8_t* as, const void* bq,
+                                 const uint8_t* bs, int64_t M, int64_t N, int64_t K, float* c,
+                                 int64_t ldc, int out_fmt, uint8_t* out_q, hipStream_t st) {
+  if (out_fmt >= 0 && out_fmt != GEMM_OUT_BF16) return hipErrorNotSupported;
+  using L = GemmLds<INT8, INT8>;
+  const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  static bool attr_done = false;  // benign race: the call is idempotent
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_i8,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  hipLaunchKernelGGL(k_gemm_i8, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), L::TOTAL, st,
+                     (const uint8_t*)aq, as, (const uint8_t*)bq, bs, M, N, K, c,
+                     out_fmt == GEMM_OUT_BF16 ? (uint16_t*)out_q : nullptr, ldc, (int)tiles_n);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // fast path (K % 512 == 0, scale arrays 16-byte aligned, operands < 4 GiB)
 //
 // A 256-thread workgroup computes a 256 x 256 tile of C.  Per stage of KS
@@ -891,6 +1032,8 @@ hipError_t launch_gemm(const void* aq, const uint8_t* as, int fa, const void* bq
                        const uint8_t* bs, int fb, int64_t M, int64_t N, int64_t K, float* c,
                        int64_t ldc, int out_fmt, uint8_t* out_q, uint8_t* out_s, hipStream_t st) {
   const MxOut mo{out_fmt, out_q, out_s};
+  if (fa == INT8 && fb == INT8)
+    return gemm_i8_launch(aq, as, bq, bs, M, N, K, c, ldc, out_fmt, out_q, st);
 #define MX_G(A, B) \
   if (fa == A && fb == B) return gemm_launch<A, B>(aq, as, bq, bs, M, N, K, c, ldc, mo, st);
 #define MX_GA(A) MX_G(A, E4M3) MX_G(A, E5M2) MX_G(A, E2M3) MX_G(A, E3M2) MX_G(A, E2M1)

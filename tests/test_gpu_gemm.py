@@ -81,6 +81,27 @@ def test_all_format_pairs_ragged(mx, oracle, fa, fb):
         assert_gemm_close(c, cref, t, f"{FMT_NAMES[fa]}x{FMT_NAMES[fb]} {M}x{N}x{K}", extra)
 
 
+def test_mxint8_gemm(mx, oracle):
+    """MXINT8 x MXINT8 (its own kernel) for K a multiple of 512 and not,
+    ragged M/N, rows of A spread over 2^-40 .. 2^40 so that block scales
+    differ widely; the products are exact, so the plain tolerance holds."""
+    rng = np.random.default_rng(77)
+    from microscaling_block_scaled_amd.synth import bf16_bits
+    for (M, N, K) in [(288, 320, 1536), (100, 36, 608), (16, 16, 32)]:
+        a = rng.standard_normal((M, K)) * np.exp2(rng.integers(-40, 41, (M, 1)))
+        a = bf16_bits(a.astype(np.float32))
+        w = bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+        (ga, oa), (gw, ow) = quant_pair(mx, oracle, a, w, 5, 5)
+        say("gemm int8", M, N, K)
+        c = host(mx.gemm(ga["q_row"], ga["s_row"], 5, gw["q_row"], gw["s_row"], 5, M, N, K))
+        cref, t = oracle.gemm_f64(oa["q_row"], oa["s_row"], 5, ow["q_row"], ow["s_row"], 5, M, N, K)
+        assert_gemm_close(c, cref, t, f"int8 {M}x{N}x{K}")
+    # mixing INT8 with a float format is refused
+    with pytest.raises(mx.MXError) as e:
+        mx.gemm(ga["q_row"], ga["s_row"], 5, gw["q_row"], gw["s_row"], 0, M, N, K)
+    assert e.value.status == mx.MX_ERR_UNSUPPORTED
+
+
 def test_ldc_and_degenerate(mx, oracle):
     rng = np.random.default_rng(3)
     from microscaling_block_scaled_amd.synth import bf16_bits

@@ -23,7 +23,7 @@ def mx():
     return m
 
 
-@pytest.mark.parametrize("fa,fb", [(0, 0), (4, 4), (1, 2)])
+@pytest.mark.parametrize("fa,fb", [(0, 0), (4, 4), (1, 2), (5, 5)])
 def test_gemm_bf16_is_rounded_fp32(mx, oracle, fa, fb):
     """Staged-kernel shapes (K % 512 == 0) and general-kernel shapes, ragged
     M/N, a leading dimension wider than N, and values spread over 2^-60 ..
@@ -84,7 +84,8 @@ def oracle_step(oracle, fmt, x, w, dy, seed, signs):
 
 
 @pytest.mark.parametrize("fmt,T,H,O", [(4, 1024, 512, 1536), (4, 288, 160, 96),
-                                       (0, 256, 512, 128), (2, 96, 64, 160)])
+                                       (0, 256, 512, 128), (2, 96, 64, 160),
+                                       (5, 288, 160, 96)])
 def test_linear_step(mx, oracle, fmt, T, H, O):
     """Forward, dgrad and wgrad of one layer; the first shape puts every
     product on the staged kernel (K = 512, 1536, 1024), the second on the
