@@ -406,10 +406,12 @@ template <int SRC> struct TileShape {
 };
 
 // Scale code and packed codes of the column block at column `col`, rows
-// rs .. rs + 31 (v: its 32 elements as fp32 bits).
+// rs .. rs + 31 (v: its 32 elements as fp32 bits).  With stochastic rounding,
+// `rw` may bring the block's 32 random words (row order); otherwise each
+// element's word is computed here.
 template <int F, bool SR, bool HAD>
 __device__ __forceinline__ uint32_t col_codes(const QP& p, uint32_t v[32], int64_t col, int64_t rs,
-                                              Pack8 o[4]) {
+                                              Pack8 o[4], const uint32_t* rw = nullptr) {
   if (HAD) {
 #pragma unroll
     for (int k = 0; k < 32; k++) v[k] = daz32(v[k]);
@@ -422,7 +424,10 @@ __device__ __forceinline__ uint32_t col_codes(const QP& p, uint32_t v[32], int64
 #pragma unroll
   for (int h = 0; h < 4; h++) {
     uint32_t rnd[8];
-    if (SR) {
+    if (SR && rw) {
+#pragma unroll
+      for (int k = 0; k < 8; k++) rnd[k] = rw[8 * h + k];
+    } else if (SR) {
 #pragma unroll
       for (int k = 0; k < 8; k++) {
         const uint64_t i = (uint64_t)((rs + 8 * h + k) * p.cols + col);
@@ -485,10 +490,41 @@ __device__ __forceinline__ void col_quad_store(const QP& p, const Pack8 o[4], ui
 }
 
 template <int F, bool SR, bool HAD>
-__device__ __forceinline__ void col_quad(const QP& p, uint32_t v[32], int64_t col, int64_t r0, int qb) {
+__device__ __forceinline__ void col_quad(const QP& p, uint32_t v[32], int64_t col, int64_t r0, int qb,
+                                         const uint32_t* rw = nullptr) {
   Pack8 o[4];
-  const uint32_t code = col_codes<F, SR, HAD>(p, v, col, r0 + 32 * qb, o);
+  const uint32_t code = col_codes<F, SR, HAD>(p, v, col, r0 + 32 * qb, o, rw);
   col_quad_store<F>(p, o, code, col, r0, qb);
+}
+
+// Stochastic-rounding words of the column pair col, col + 1 (col even) for
+// rows rs .. rs + 31, in row order (rw[k][row] for column col + k).  One
+// Philox call gives the words of a row's group of four columns (the source
+// tensor's element index i = row * cols + col, cols % 4 == 0), whose other
+// pair the lane ^ 4 holds for the same rows.  So each of the two lanes makes
+// the calls of 16 rows and hands the other its two words of each: a quarter
+// of the calls of one call per element.  Needs every lane of the wave active.
+__device__ __forceinline__ void sr_pair_words(const QP& p, int64_t col, int64_t rs,
+                                              uint32_t (&rw)[2][32]) {
+  const bool hi = (col >> 1) & 1;  // second pair of its group of four
+  const int64_t g0 = col & ~(int64_t)3;
+#pragma unroll
+  for (int j = 0; j < 16; j++) {
+    // this lane's calls: rows 16 hi + j
+    const int64_t row = rs + (hi ? 16 : 0) + j;
+    const U4 w = sr_words(p.seed, p.off, 1u, (uint64_t)(row * p.cols + g0) >> 2);
+    uint32_t own0 = hi ? w.z : w.x, own1 = hi ? w.w : w.y;
+    uint32_t oth0 = hi ? w.x : w.z, oth1 = hi ? w.y : w.w;
+    asm volatile("" : "+v"(oth0), "+v"(oth1));
+    // bit-mask swizzle: lane ^ 4 within each group of 32
+    const uint32_t in0 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)oth0, 0x101F);
+    const uint32_t in1 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)oth1, 0x101F);
+    // rows j (first half) and 16 + j (second half)
+    rw[0][j] = hi ? in0 : own0;
+    rw[1][j] = hi ? in1 : own1;
+    rw[0][16 + j] = hi ? own0 : in0;
+    rw[1][16 + j] = hi ? own1 : in1;
+  }
 }
 
 // Whole-tile column pass on bf16 pairs without stochastic rounding or the
@@ -638,13 +674,18 @@ __global__ __launch_bounds__(256) void k_quant_tiles(QP p) {
     if constexpr (FASTCOL) {
       col_pair_bf16<F>(p, w, c0 + 2 * d, r0, qb);
     } else {
+      // bf16 with SR: the lane's two columns' random words come from one
+      // Philox call per row, shared with the lane holding the neighbouring pair
+      uint32_t rw[2][32];
+      constexpr bool PAIRED = SR && T::CPT == 2;
+      if constexpr (PAIRED) sr_pair_words(p, c0 + 2 * d, r0 + 32 * qb, rw);
 #pragma unroll
       for (int k = 0; k < T::CPT; k++) {
         uint32_t v[32];
 #pragma unroll
         for (int i = 0; i < 32; i++)
           v[i] = SRC == SRC_BF16 ? (k == 0 ? w[i] << 16 : w[i] & 0xFFFF0000u) : w[i];
-        col_quad<F, SR, HAD>(p, v, c0 + T::CPT * d + k, r0, qb);
+        col_quad<F, SR, HAD>(p, v, c0 + T::CPT * d + k, r0, qb, PAIRED ? rw[k] : nullptr);
       }
     }
   } else {
