@@ -32,6 +32,7 @@ namespace mx {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int BM = 256, BN = 256, KS = 128;
 
@@ -249,8 +250,6 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ aq,
 // block, which the vector ALU cannot keep up with.  Values of blocks with scale
 // codes below 7 fall below bf16's normal range and round; their contribution
 // is below 2^-120 per product.
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-
 // 8 INT8 codes (w: bytes 0..7 = elements 0..7) of one block with scale code
 // s, as bf16 values n * 2^(s - 133).
 __device__ __forceinline__ v8bf i8_bf16(uint2 w, int s) {
@@ -548,12 +547,19 @@ __device__ __forceinline__ void read_scale_words(ScaleWords<C::KS>& sw, const ui
 }
 
 // Scale operands of substep u: byte 2u + kb of the stage's bytes of the row.
-template <int KS>
+// For MXINT8 (I8) both of the substep's scale bytes, 2u and 2u + 1, as the
+// low 16 bits: a lane's operand bytes come from both of its blocks.
+template <int KS, bool I8 = false>
 __device__ __forceinline__ void scales_of(Ops& o, const ScaleWords<KS>& sw, int u, const Lanes& w) {
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    o.sa[i] = (int)__builtin_amdgcn_ubfe(sw.a[i][u / 2], w.bsh[u & 1], 8);
-    o.sb[i] = (int)__builtin_amdgcn_ubfe(sw.b[i][u / 2], w.bsh[u & 1], 8);
+    if (I8) {
+      o.sa[i] = (int)__builtin_amdgcn_ubfe(sw.a[i][u / 2], 16 * (u & 1), 16);
+      o.sb[i] = (int)__builtin_amdgcn_ubfe(sw.b[i][u / 2], 16 * (u & 1), 16);
+    } else {
+      o.sa[i] = (int)__builtin_amdgcn_ubfe(sw.a[i][u / 2], w.bsh[u & 1], 8);
+      o.sb[i] = (int)__builtin_amdgcn_ubfe(sw.b[i][u / 2], w.bsh[u & 1], 8);
+    }
   }
 }
 
@@ -589,6 +595,35 @@ __device__ __forceinline__ void substep(v16f (&acc)[4][4], const Ops& cur, Slot&
                                                                 0, cur.sb[j], 0, cur.sa[i]);
     slot(K);
     __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+// One MXINT8 substep on the same operand registers: a lane's 32 bytes are 16
+// of block 2u (K offsets 16 kb ..) and 16 of block 2u + 1 (32 + 16 kb ..).
+// Four slices t of 8 bytes each become bf16 with their block's scale folded
+// in (i8_bf16) and feed 16 bf16 32x32x16 instructions.  A and B lanes take
+// the same K positions in the same slice, so the four slices together cover
+// the substep's 64 products of every (row, column) pair exactly once, in a
+// different order from the block-scaled instruction.  slot(k) follows every
+// fourth instruction, in order.
+template <class Slot>
+__device__ __forceinline__ void substep_i8(v16f (&acc)[4][4], const Ops& cur, Slot&& slot) {
+  static_for<4>([&](auto T) {
+    constexpr int t = decltype(T)::value;
+    v8bf a8[4], b8[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int sa = t < 2 ? (cur.sa[i] & 0xFF) : ((cur.sa[i] >> 8) & 0xFF);
+      const int sb = t < 2 ? (cur.sb[i] & 0xFF) : ((cur.sb[i] >> 8) & 0xFF);
+      a8[i] = i8_bf16(make_uint2((uint32_t)cur.a[i][2 * t], (uint32_t)cur.a[i][2 * t + 1]), sa);
+      b8[i] = i8_bf16(make_uint2((uint32_t)cur.b[i][2 * t], (uint32_t)cur.b[i][2 * t + 1]), sb);
+    }
+    static_for<16>([&](auto K) {
+      constexpr int k = decltype(K)::value, i = k >> 2, j = k & 3;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b8[j], a8[i], acc[i][j], 0, 0, 0);
+      if constexpr (k % 4 == 3) slot(std::integral_constant<int, 4 * t + k / 4>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
   });
 }
 
@@ -865,7 +900,7 @@ __global__ __launch_bounds__(256) void k_gemm_fast(const uint8_t* __restrict__ a
   read_scale_words<C, FA, FB>(sw, lds, 0, w);
   static_for<RA>([&](auto R) {
     constexpr int r = decltype(R)::value;
-    scales_of<KS>(ops[r], sw, r, w);
+    scales_of<KS, FA == INT8>(ops[r], sw, r, w);
 #pragma unroll
     for (int t = 0; t < 8; t++) read_tile<C, FA, FB>(ops[r], slot(0), r, t, w);
   });
@@ -892,7 +927,7 @@ __global__ __launch_bounds__(256) void k_gemm_fast(const uint8_t* __restrict__ a
       constexpr bool next = u + RA >= SUB;   // ... of stage s + 1
       Ops& nxt = ops[(u + RA) % NB];
       const uint8_t* st = next ? slot(s + 1) : slot(s);
-      substep<FA, FB>(acc, ops[u % NB], [&](auto K) {
+      auto body = [&](auto K) {
         constexpr int k = decltype(K)::value;
         if constexpr (u == SU && k == SK) {
           wait_all_barrier<AHEAD>();
@@ -906,11 +941,15 @@ __global__ __launch_bounds__(256) void k_gemm_fast(const uint8_t* __restrict__ a
             if constexpr ((j * NSLOT) / NLD == g) issue_one(s + NST, j);
           });
         }
-      });
-      if constexpr (next)
-        scales_of<KS>(nxt, swn, un, w);
+      };
+      if constexpr (FA == INT8)
+        substep_i8(acc, ops[u % NB], body);
       else
-        scales_of<KS>(nxt, sw, un, w);
+        substep<FA, FB>(acc, ops[u % NB], body);
+      if constexpr (next)
+        scales_of<KS, FA == INT8>(nxt, swn, un, w);
+      else
+        scales_of<KS, FA == INT8>(nxt, sw, un, w);
     });
     sw = swn;
   }
@@ -1014,26 +1053,29 @@ static hipError_t gemm_launch(const void* aq, const uint8_t* as, const void* bq,
       return launch_fast<FA, FB, 128>(aq, as, bq, bs, M, N, K, c, ldc, tiles_m, tiles_n, mo, st);
   }
   if (mo.fmt >= 0 && mo.fmt != GEMM_OUT_BF16) return hipErrorNotSupported;  // MX output: staged only
-  using L = GemmLds<FA, FB>;
-  static bool attr_done = false;  // benign race: the call is idempotent
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm<FA, FB>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
-    if (e != hipSuccess) return e;
-    attr_done = true;
+  if constexpr (FA == INT8) {
+    return gemm_i8_launch(aq, as, bq, bs, M, N, K, c, ldc, mo.fmt, mo.q, st);
+  } else {
+    using L = GemmLds<FA, FB>;
+    static bool attr_done = false;  // benign race: the call is idempotent
+    if (!attr_done) {
+      hipError_t e = hipFuncSetAttribute((const void*)k_gemm<FA, FB>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
+      if (e != hipSuccess) return e;
+      attr_done = true;
+    }
+    hipLaunchKernelGGL((k_gemm<FA, FB>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), L::TOTAL,
+                       st, (const uint8_t*)aq, as, (const uint8_t*)bq, bs, M, N, K, c,
+                       mo.fmt == GEMM_OUT_BF16 ? (uint16_t*)mo.q : nullptr, ldc, (int)tiles_n);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL((k_gemm<FA, FB>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), L::TOTAL, st,
-                     (const uint8_t*)aq, as, (const uint8_t*)bq, bs, M, N, K, c,
-                     mo.fmt == GEMM_OUT_BF16 ? (uint16_t*)mo.q : nullptr, ldc, (int)tiles_n);
-  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const void* aq, const uint8_t* as, int fa, const void* bq,
                        const uint8_t* bs, int fb, int64_t M, int64_t N, int64_t K, float* c,
                        int64_t ldc, int out_fmt, uint8_t* out_q, uint8_t* out_s, hipStream_t st) {
   const MxOut mo{out_fmt, out_q, out_s};
-  if (fa == INT8 && fb == INT8)
-    return gemm_i8_launch(aq, as, bq, bs, M, N, K, c, ldc, out_fmt, out_q, st);
+  if (fa == INT8 && fb == INT8) return gemm_launch<INT8, INT8>(aq, as, bq, bs, M, N, K, c, ldc, mo, st);
 #define MX_G(A, B) \
   if (fa == A && fb == B) return gemm_launch<A, B>(aq, as, bq, bs, M, N, K, c, ldc, mo, st);
 #define MX_GA(A) MX_G(A, E4M3) MX_G(A, E5M2) MX_G(A, E2M3) MX_G(A, E3M2) MX_G(A, E2M1)
