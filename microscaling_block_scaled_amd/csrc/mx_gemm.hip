@@ -608,9 +608,7 @@ __device__ __forceinline__ void substep(v16f (&acc)[4][4], const Ops& cur, Slot&
 // fourth instruction, in order.
 template <class Slot>
 __device__ __forceinline__ void substep_i8(v16f (&acc)[4][4], const Ops& cur, Slot&& slot) {
-  static_for<4>([&](auto T) {
-    constexpr int t = decltype(T)::value;
-    v8bf a8[4], b8[4];
+  auto convert = [&](int t, v8bf (&a8)[4], v8bf (&b8)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int sa = t < 2 ? (cur.sa[i] & 0xFF) : ((cur.sa[i] >> 8) & 0xFF);
@@ -618,11 +616,18 @@ __device__ __forceinline__ void substep_i8(v16f (&acc)[4][4], const Ops& cur, Sl
       a8[i] = i8_bf16(make_uint2((uint32_t)cur.a[i][2 * t], (uint32_t)cur.a[i][2 * t + 1]), sa);
       b8[i] = i8_bf16(make_uint2((uint32_t)cur.b[i][2 * t], (uint32_t)cur.b[i][2 * t + 1]), sb);
     }
+  };
+  // the operands of slice t + 1 are converted within slice t's last group of
+  // instructions, where the scheduler can place them under the matrix work
+  v8bf a8[2][4], b8[2][4];
+  convert(0, a8[0], b8[0]);
+  static_for<4>([&](auto T) {
+    constexpr int t = decltype(T)::value, c = t & 1;
     static_for<16>([&](auto K) {
       constexpr int k = decltype(K)::value, i = k >> 2, j = k & 3;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b8[j], a8[i], acc[i][j], 0, 0, 0);
+      if constexpr (k == 12 && t < 3) convert(t + 1, a8[c ^ 1], b8[c ^ 1]);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b8[c][j], a8[c][i], acc[i][j], 0, 0, 0);
       if constexpr (k % 4 == 3) slot(std::integral_constant<int, 4 * t + k / 4>{});
-      __builtin_amdgcn_sched_barrier(0);
     });
   });
 }
