@@ -406,12 +406,10 @@ template <int SRC> struct TileShape {
 };
 
 // Scale code and packed codes of the column block at column `col`, rows
-// rs .. rs + 31 (v: its 32 elements as fp32 bits).  With stochastic rounding,
-// `rw` may bring the block's 32 random words (row order); otherwise each
-// element's word is computed here.
+// rs .. rs + 31 (v: its 32 elements as fp32 bits).
 template <int F, bool SR, bool HAD>
 __device__ __forceinline__ uint32_t col_codes(const QP& p, uint32_t v[32], int64_t col, int64_t rs,
-                                              Pack8 o[4], const uint32_t* rw = nullptr) {
+                                              Pack8 o[4]) {
   if (HAD) {
 #pragma unroll
     for (int k = 0; k < 32; k++) v[k] = daz32(v[k]);
@@ -424,10 +422,7 @@ __device__ __forceinline__ uint32_t col_codes(const QP& p, uint32_t v[32], int64
 #pragma unroll
   for (int h = 0; h < 4; h++) {
     uint32_t rnd[8];
-    if (SR && rw) {
-#pragma unroll
-      for (int k = 0; k < 8; k++) rnd[k] = rw[8 * h + k];
-    } else if (SR) {
+    if (SR) {
 #pragma unroll
       for (int k = 0; k < 8; k++) {
         const uint64_t i = (uint64_t)((rs + 8 * h + k) * p.cols + col);
@@ -490,40 +485,89 @@ __device__ __forceinline__ void col_quad_store(const QP& p, const Pack8 o[4], ui
 }
 
 template <int F, bool SR, bool HAD>
-__device__ __forceinline__ void col_quad(const QP& p, uint32_t v[32], int64_t col, int64_t r0, int qb,
-                                         const uint32_t* rw = nullptr) {
+__device__ __forceinline__ void col_quad(const QP& p, uint32_t v[32], int64_t col, int64_t r0, int qb) {
   Pack8 o[4];
-  const uint32_t code = col_codes<F, SR, HAD>(p, v, col, r0 + 32 * qb, o, rw);
+  const uint32_t code = col_codes<F, SR, HAD>(p, v, col, r0 + 32 * qb, o);
   col_quad_store<F>(p, o, code, col, r0, qb);
 }
 
-// Stochastic-rounding words of the column pair col, col + 1 (col even) for
-// rows rs .. rs + 31, in row order (rw[k][row] for column col + k).  One
-// Philox call gives the words of a row's group of four columns (the source
-// tensor's element index i = row * cols + col, cols % 4 == 0), whose other
-// pair the lane ^ 4 holds for the same rows.  So each of the two lanes makes
-// the calls of 16 rows and hands the other its two words of each: a quarter
-// of the calls of one call per element.  Needs every lane of the wave active.
-__device__ __forceinline__ void sr_pair_words(const QP& p, int64_t col, int64_t rs,
-                                              uint32_t (&rw)[2][32]) {
+// Column pass on bf16 pairs with stochastic rounding: w[i] holds columns col
+// (low half, col even) and col + 1 (high half) of row rs + i.  One Philox call
+// gives the words of a row's group of four columns (element index i = row *
+// cols + col with cols % 4 == 0), so one call serves both columns.  In whole
+// tiles (WHOLE, rs = r0 + 32 qb) the lane ^ 4 holds the group's other pair
+// for the same rows: per 8-row chunk each lane of the pair makes the calls of
+// four rows and hands the other its two words of each (a quarter of the calls
+// of one call per element; needs every lane of the wave active), and the
+// codes go out through the quad exchange.  Ragged tiles make all of a chunk's
+// calls themselves and store plainly.  Both columns' scale codes come first;
+// the chunks then convert both columns, so only one chunk's words are live.
+template <int F, bool HAD, bool WHOLE>
+__device__ __forceinline__ void col_pair_sr(const QP& p, const uint32_t w[32], int64_t col, int64_t r0,
+                                            int qb) {
+  const int64_t rs = r0 + 32 * qb;
+  uint32_t v[2][32];
+#pragma unroll
+  for (int i = 0; i < 32; i++) {
+    v[0][i] = w[i] << 16;
+    v[1][i] = w[i] & 0xFFFF0000u;
+  }
+  uint32_t code[2];
+#pragma unroll
+  for (int k = 0; k < 2; k++) {
+    if (HAD) {
+#pragma unroll
+      for (int i = 0; i < 32; i++) v[k][i] = daz32(v[k][i]);
+      hadamard_local(v[k], p.signs);
+    }
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 32; i++) am = umax(am, v[k][i] & 0x7FFFFFFFu);
+    code[k] = scale_code<F>(am);
+  }
   const bool hi = (col >> 1) & 1;  // second pair of its group of four
   const int64_t g0 = col & ~(int64_t)3;
+  Pack8 o[2][4];
 #pragma unroll
-  for (int j = 0; j < 16; j++) {
-    // this lane's calls: rows 16 hi + j
-    const int64_t row = rs + (hi ? 16 : 0) + j;
-    const U4 w = sr_words(p.seed, p.off, 1u, (uint64_t)(row * p.cols + g0) >> 2);
-    uint32_t own0 = hi ? w.z : w.x, own1 = hi ? w.w : w.y;
-    uint32_t oth0 = hi ? w.x : w.z, oth1 = hi ? w.y : w.w;
-    asm volatile("" : "+v"(oth0), "+v"(oth1));
-    // bit-mask swizzle: lane ^ 4 within each group of 32
-    const uint32_t in0 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)oth0, 0x101F);
-    const uint32_t in1 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)oth1, 0x101F);
-    // rows j (first half) and 16 + j (second half)
-    rw[0][j] = hi ? in0 : own0;
-    rw[1][j] = hi ? in1 : own1;
-    rw[0][16 + j] = hi ? own0 : in0;
-    rw[1][16 + j] = hi ? own1 : in1;
+  for (int h = 0; h < 4; h++) {
+    uint32_t rnd[2][8];
+    if constexpr (!WHOLE) {
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const U4 wd = sr_words(p.seed, p.off, 1u, (uint64_t)((rs + 8 * h + j) * p.cols + g0) >> 2);
+        rnd[0][j] = hi ? wd.z : wd.x;
+        rnd[1][j] = hi ? wd.w : wd.y;
+      }
+    } else {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      // this lane's calls: chunk rows 4 hi + j; the partner's: 4 (1 - hi) + j
+      const int64_t row = rs + 8 * h + (hi ? 4 : 0) + j;
+      const U4 wd = sr_words(p.seed, p.off, 1u, (uint64_t)(row * p.cols + g0) >> 2);
+      const uint32_t own0 = hi ? wd.z : wd.x, own1 = hi ? wd.w : wd.y;
+      uint32_t oth0 = hi ? wd.x : wd.z, oth1 = hi ? wd.y : wd.w;
+      asm volatile("" : "+v"(oth0), "+v"(oth1));
+      // bit-mask swizzle: lane ^ 4 within each group of 32
+      const uint32_t in0 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)oth0, 0x101F);
+      const uint32_t in1 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)oth1, 0x101F);
+      rnd[0][j] = hi ? in0 : own0;
+      rnd[1][j] = hi ? in1 : own1;
+      rnd[0][4 + j] = hi ? own0 : in0;
+      rnd[1][4 + j] = hi ? own1 : in1;
+    }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; k++) o[k][h] = convert8<F, true>(&v[k][8 * h], code[k], rnd[k]);
+  }
+  if constexpr (WHOLE) {
+    col_quad_store<F>(p, o[0], code[0], col, r0, qb);
+    col_quad_store<F>(p, o[1], code[1], col + 1, r0, qb);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+      p.s_colt[(col + k) * (p.rows >> 5) + (rs >> 5)] = (uint8_t)code[k];
+      store32<F>(p.q_colt + (col + k) * p.qc_pitch + (rs * Fmt<F>::bits) / 8, o[k]);
+    }
   }
 }
 
@@ -593,7 +637,7 @@ __device__ __forceinline__ int tile_swz(int r) { return ((r >> 5) & 3) * 4; }
 // columns (one 128-byte transposed line each for 8-bit codes).  Ragged edge
 // tiles: wave qb takes rows 32 qb .., lane g the dword g.
 template <int SRC, int F, bool SR, bool HAD, bool ROWS>
-__global__ __launch_bounds__(256) void k_quant_tiles(QP p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SR && SRC == SRC_BF16 ? 3 : 1))) void k_quant_tiles(QP p) {
   using T = TileShape<SRC>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[T::TR * T::ROWB];
   __shared__ uint32_t sc_lds[T::TR];  // row-wise scale bytes of a whole tile, one dword per row
@@ -673,19 +717,16 @@ __global__ __launch_bounds__(256) void k_quant_tiles(QP p) {
     for (int i = 0; i < 32; i++) w[i] = *(const uint32_t*)(src + i * T::ROWB);
     if constexpr (FASTCOL) {
       col_pair_bf16<F>(p, w, c0 + 2 * d, r0, qb);
+    } else if constexpr (SR && SRC == SRC_BF16) {
+      col_pair_sr<F, HAD, true>(p, w, c0 + 2 * d, r0, qb);
     } else {
-      // bf16 with SR: the lane's two columns' random words come from one
-      // Philox call per row, shared with the lane holding the neighbouring pair
-      uint32_t rw[2][32];
-      constexpr bool PAIRED = SR && T::CPT == 2;
-      if constexpr (PAIRED) sr_pair_words(p, c0 + 2 * d, r0 + 32 * qb, rw);
 #pragma unroll
       for (int k = 0; k < T::CPT; k++) {
         uint32_t v[32];
 #pragma unroll
         for (int i = 0; i < 32; i++)
           v[i] = SRC == SRC_BF16 ? (k == 0 ? w[i] << 16 : w[i] & 0xFFFF0000u) : w[i];
-        col_quad<F, SR, HAD>(p, v, c0 + T::CPT * d + k, r0, qb, PAIRED ? rw[k] : nullptr);
+        col_quad<F, SR, HAD>(p, v, c0 + T::CPT * d + k, r0, qb);
       }
     }
   } else {
@@ -694,13 +735,17 @@ __global__ __launch_bounds__(256) void k_quant_tiles(QP p) {
       uint32_t w[32];
 #pragma unroll
       for (int i = 0; i < 32; i++) w[i] = *(const uint32_t*)(lds + (32 * qb + i) * T::ROWB + g * 4);
+      if constexpr (SR && SRC == SRC_BF16) {
+        col_pair_sr<F, HAD, false>(p, w, c0 + 2 * g, r0, qb);
+      } else {
 #pragma unroll
-      for (int k = 0; k < T::CPT; k++) {
-        uint32_t v[32];
+        for (int k = 0; k < T::CPT; k++) {
+          uint32_t v[32];
 #pragma unroll
-        for (int i = 0; i < 32; i++)
-          v[i] = SRC == SRC_BF16 ? (k == 0 ? w[i] << 16 : w[i] & 0xFFFF0000u) : w[i];
-        col_block<F, SR, HAD>(p, v, c0 + g * T::CPT + k, r0 + 32 * qb);
+          for (int i = 0; i < 32; i++)
+            v[i] = SRC == SRC_BF16 ? (k == 0 ? w[i] << 16 : w[i] & 0xFFFF0000u) : w[i];
+          col_block<F, SR, HAD>(p, v, c0 + g * T::CPT + k, r0 + 32 * qb);
+        }
       }
     }
   }
