@@ -23,8 +23,9 @@
  *
  * Conventions for every entry point:
  *   - All data pointers are DEVICE pointers, owned by the caller.  The library
- *     never allocates or frees memory and keeps no mutable global state; calls
- *     are thread-safe.
+ *     never allocates or frees memory; its only global state is a kernel
+ *     attribute (the general GEMM kernels' LDS size) set once on first use,
+ *     idempotently, so calls are thread-safe.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *     default stream).  Device faults surface at the caller's next
  *     synchronization on that stream.
