@@ -136,7 +136,9 @@ def quantize(x: np.ndarray, fmt: int, layouts: int = LAYOUT_ROW, round_mode: int
              flags: int = 0, seed: int = 0, counter_offset: int = 0, hadamard_signs: int = 0,
              src: int | None = None):
     """Quantize a 2-D array.  ``x`` is float32, or uint16 holding bf16 bit
-    patterns.  Returns dict with q_row/s_row and/or q_colt/s_colt (uint8)."""
+    patterns.  Returns dict with q_row/s_row and/or q_colt/s_colt (uint8).  A
+    blocked dimension that is not a multiple of 32 is quantized as if padded
+    with zeros to the next multiple (the outputs keep the padded blocks)."""
     if src is None:
         src = SRC_F32 if x.dtype == np.float32 else SRC_BF16
     want = np.float32 if src == SRC_F32 else np.uint16
@@ -146,11 +148,11 @@ def quantize(x: np.ndarray, fmt: int, layouts: int = LAYOUT_ROW, round_mode: int
     q_row = s_row = q_colt = s_colt = None
     if layouts & LAYOUT_ROW:
         q_row = np.zeros((rows, packed_bytes(fmt, 1, cols)), np.uint8)
-        s_row = np.zeros((rows, cols // 32), np.uint8)
+        s_row = np.zeros((rows, (cols + 31) // 32), np.uint8)
         out["q_row"], out["s_row"] = q_row, s_row
     if layouts & LAYOUT_COLT:
         q_colt = np.zeros((cols, packed_bytes(fmt, 1, rows)), np.uint8)
-        s_colt = np.zeros((cols, rows // 32), np.uint8)
+        s_colt = np.zeros((cols, (rows + 31) // 32), np.uint8)
         out["q_colt"], out["s_colt"] = q_colt, s_colt
     p = lambda a: None if a is None else _ptr(a)
     rc = _load().mxo_quantize(src, _ptr(x), rows, cols, cols, fmt, layouts, round_mode, flags,

@@ -22,7 +22,12 @@
  *     element's 32-bit Philox word and F = floor(frac * 2^32) for the discarded
  *     fraction frac of one grid step;
  *   - subnormal fp32 values are flushed to signed zero when loaded and again at
- *     the input of the block conversion (after the optional Hadamard step).
+ *     the input of the block conversion (after the optional Hadamard step);
+ *   - a blocked dimension that is not a multiple of 32 is padded with zeros to
+ *     the next multiple (the pages fix no convention for a short block): the
+ *     missing elements of the last block read as +0, the packed row holds the
+ *     whole padded block, and stochastic-rounding indices are taken in the
+ *     padded tensor.
  */
 #include "mx_oracle.h"
 
@@ -234,12 +239,16 @@ void mxo_hadamard32(float x[32], uint32_t signs) {
 /* ------------------------------------------------------------------------- */
 /* Packing.                                                                   */
 /* ------------------------------------------------------------------------- */
+/* n rounded up to whole 32-element blocks */
+static int64_t padded(int64_t n) { return (n + 31) / 32 * 32; }
+
 int64_t mxo_packed_bytes(int fmt, int64_t rows, int64_t cols) {
   if (!fmt_ok(fmt) || rows < 0 || cols < 0) return -1;
-  return rows * (cols * FMTS[fmt].bits / 8);
+  return rows * (padded(cols) * FMTS[fmt].bits / 8);
 }
 
-static int64_t row_bytes(int fmt, int64_t cols) { return cols * FMTS[fmt].bits / 8; }
+/* bytes of one packed row of `cols` elements (a whole number of blocks) */
+static int64_t row_bytes(int fmt, int64_t cols) { return padded(cols) * FMTS[fmt].bits / 8; }
 
 static void put_code(uint8_t* row, int fmt, int64_t j, uint8_t code) {
   int bits = FMTS[fmt].bits;
@@ -282,14 +291,17 @@ static float load_elem(int src, const void* x, int64_t idx) {
   return v;
 }
 
-/* One block: 32 source elements (strided), optional Hadamard, Algorithm 1. */
-static void quantize_one(int src, const void* x, int64_t base, int64_t stride, int fmt, int round,
-                         unsigned flags, uint64_t seed, uint64_t off, uint32_t signs, int layout_id,
-                         int64_t logical0, int64_t logical_stride, uint8_t codes[32],
+/* One block: 32 source elements (strided), of which the first `valid` exist
+ * and the rest are the zero padding of a short last block; optional Hadamard,
+ * Algorithm 1. */
+static void quantize_one(int src, const void* x, int64_t base, int64_t stride, int valid, int fmt,
+                         int round, unsigned flags, uint64_t seed, uint64_t off, uint32_t signs,
+                         int layout_id, int64_t logical0, int64_t logical_stride, uint8_t codes[32],
                          uint8_t* scale) {
   float v[32];
   uint32_t rnd[32];
-  for (int k = 0; k < 32; k++) v[k] = flush_subnormal(load_elem(src, x, base + k * stride));
+  for (int k = 0; k < 32; k++)
+    v[k] = k < valid ? flush_subnormal(load_elem(src, x, base + k * stride)) : 0.0f;
   if (flags & MXO_FLAG_HADAMARD32) mxo_hadamard32(v, signs);
   if (round == MXO_SR)
     for (int k = 0; k < 32; k++)
@@ -306,31 +318,36 @@ int mxo_quantize(int src, const void* x, int64_t rows, int64_t cols, int64_t ld,
   if (rows < 0 || cols < 0 || ld < cols) return -1;
   if ((layouts & ~3u) || layouts == 0) return -1;
 
+  /* logical (stochastic-rounding) index of element (r, c): r * cp + c in the
+   * zero-padded tensor */
+  const int64_t cp = padded(cols);
   if (layouts & MXO_LAYOUT_ROW) {
-    if (cols % 32 || !q_row || !s_row) return -1;
-    int64_t nb = cols / 32, rb = row_bytes(fmt, cols);
+    if (!q_row || !s_row) return -1;
+    int64_t nb = cp / 32, rb = row_bytes(fmt, cols);
     memset(q_row, 0, (size_t)(rows * rb));
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; r++) {
       for (int64_t b = 0; b < nb; b++) {
         uint8_t codes[32], sc;
-        quantize_one(src, x, r * ld + b * 32, 1, fmt, round, flags, seed, counter_offset,
-                     hadamard_signs, 0, r * cols + b * 32, 1, codes, &sc);
+        const int valid = (int)(cols - b * 32 < 32 ? cols - b * 32 : 32);
+        quantize_one(src, x, r * ld + b * 32, 1, valid, fmt, round, flags, seed, counter_offset,
+                     hadamard_signs, 0, r * cp + b * 32, 1, codes, &sc);
         s_row[r * nb + b] = sc;
         for (int k = 0; k < 32; k++) put_code(q_row + r * rb, fmt, b * 32 + k, codes[k]);
       }
     }
   }
   if (layouts & MXO_LAYOUT_COLT) {
-    if (rows % 32 || !q_colt || !s_colt) return -1;
-    int64_t nb = rows / 32, rb = row_bytes(fmt, rows);
+    if (!q_colt || !s_colt) return -1;
+    int64_t nb = padded(rows) / 32, rb = row_bytes(fmt, rows);
     memset(q_colt, 0, (size_t)(cols * rb));
 #pragma omp parallel for schedule(static)
     for (int64_t c = 0; c < cols; c++) {
       for (int64_t b = 0; b < nb; b++) {
         uint8_t codes[32], sc;
-        quantize_one(src, x, b * 32 * ld + c, ld, fmt, round, flags, seed, counter_offset,
-                     hadamard_signs, 1, b * 32 * cols + c, cols, codes, &sc);
+        const int valid = (int)(rows - b * 32 < 32 ? rows - b * 32 : 32);
+        quantize_one(src, x, b * 32 * ld + c, ld, valid, fmt, round, flags, seed, counter_offset,
+                     hadamard_signs, 1, b * 32 * cp + c, cp, codes, &sc);
         s_colt[c * nb + b] = sc;
         for (int k = 0; k < 32; k++) put_code(q_colt + c * rb, fmt, b * 32 + k, codes[k]);
       }
@@ -339,10 +356,11 @@ int mxo_quantize(int src, const void* x, int64_t rows, int64_t cols, int64_t ld,
   return 0;
 }
 
-/* value of element (r, j) of a packed tensor, with its block scale, in fp64 */
+/* value of element (r, j) of a packed tensor of `cols` elements per row
+ * (blocks along the row, padded), with its block scale, in fp64 */
 static double deq_elem(const uint8_t* q, const uint8_t* s, int fmt, int64_t cols, int64_t r,
                        int64_t j) {
-  uint8_t sc = s[r * (cols / 32) + j / 32];
+  uint8_t sc = s[r * (padded(cols) / 32) + j / 32];
   if (sc == 0xFF) return NAN; /* NaN scale: the whole block is NaN */
   double p = mxo_elem_value(fmt, get_code(q + r * row_bytes(fmt, cols), fmt, j));
   return ldexp(p, (int)sc - 127); /* v = X * P, exact in fp64 */
@@ -350,7 +368,7 @@ static double deq_elem(const uint8_t* q, const uint8_t* s, int fmt, int64_t cols
 
 int mxo_dequantize(const uint8_t* q, const uint8_t* s, int fmt, int64_t rows, int64_t cols,
                    float* y) {
-  if (!fmt_ok(fmt) || rows < 0 || cols < 0 || cols % 32) return -1;
+  if (!fmt_ok(fmt) || rows < 0 || cols < 0) return -1;
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; r++)
     for (int64_t j = 0; j < cols; j++)
@@ -358,11 +376,13 @@ int mxo_dequantize(const uint8_t* q, const uint8_t* s, int fmt, int64_t rows, in
   return 0;
 }
 
+/* sum over the whole padded length of K: the padded positions hold whatever
+ * the operands' last blocks hold there */
 static void dot_f64(const uint8_t* a_q, const uint8_t* a_s, int a_fmt, const uint8_t* b_q,
                     const uint8_t* b_s, int b_fmt, int64_t K, int64_t m, int64_t n, double* c,
                     double* t) {
   double acc = 0.0, abs_acc = 0.0;
-  for (int64_t k = 0; k < K; k++) {
+  for (int64_t k = 0; k < padded(K); k++) {
     double p = deq_elem(a_q, a_s, a_fmt, K, m, k) * deq_elem(b_q, b_s, b_fmt, K, n, k);
     acc += p;
     abs_acc += fabs(p);
@@ -374,7 +394,7 @@ static void dot_f64(const uint8_t* a_q, const uint8_t* a_s, int a_fmt, const uin
 int mxo_gemm_f64(const uint8_t* a_q, const uint8_t* a_s, int a_fmt, const uint8_t* b_q,
                  const uint8_t* b_s, int b_fmt, int64_t M, int64_t N, int64_t K, double* c,
                  double* t) {
-  if (!fmt_ok(a_fmt) || !fmt_ok(b_fmt) || M < 0 || N < 0 || K < 0 || K % 32) return -1;
+  if (!fmt_ok(a_fmt) || !fmt_ok(b_fmt) || M < 0 || N < 0 || K < 0) return -1;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t m = 0; m < M; m++)
     for (int64_t n = 0; n < N; n++)
@@ -385,7 +405,7 @@ int mxo_gemm_f64(const uint8_t* a_q, const uint8_t* a_s, int a_fmt, const uint8_
 int mxo_gemm_f64_at(const uint8_t* a_q, const uint8_t* a_s, int a_fmt, const uint8_t* b_q,
                     const uint8_t* b_s, int b_fmt, int64_t M, int64_t N, int64_t K,
                     const int64_t* ms, const int64_t* ns, int64_t count, double* c, double* t) {
-  if (!fmt_ok(a_fmt) || !fmt_ok(b_fmt) || K < 0 || K % 32) return -1;
+  if (!fmt_ok(a_fmt) || !fmt_ok(b_fmt) || K < 0) return -1;
   for (int64_t i = 0; i < count; i++)
     if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N) return -1;
 #pragma omp parallel for schedule(dynamic, 16)

@@ -32,6 +32,14 @@
  * those of the public OCP MX v1.0 / OCP 8-bit floating point definitions; the
  * pages name the formats but do not print them.
  *
+ * Partial blocks: the pages define blocks of k elements and leave the storage
+ * to the implementation.  A blocked dimension n that is not a multiple of 32
+ * is taken as the tensor extended with zeros to n_p = 32 * ceil(n / 32): the
+ * packed outputs hold n_p elements per row (padded positions included) and
+ * n_p / 32 scales, the logical index of an element for stochastic rounding is
+ * row * C_p + col with C_p = 32 * ceil(cols / 32), and a dot product runs over
+ * the padded length.  For n % 32 == 0 nothing changes.
+ *
  * Every pointer here is a HOST pointer.  Byte arrays hold packed element codes
  * exactly as the GPU library stores them (FP8/INT8: one byte per element;
  * FP6: 24 bytes per 32-element block, element j in bits 6j..6j+5 of the
@@ -78,26 +86,30 @@ uint32_t mxo_sr_word(uint64_t seed, uint64_t counter_offset, int layout_id, uint
 /* Fixed-sign 32-point Hadamard transform in fp32, in place. */
 void mxo_hadamard32(float x[32], uint32_t signs);
 
-/* Packed bytes for a [rows x cols] element array whose blocks run along cols. */
+/* Packed bytes for a [rows x cols] element array whose blocks run along cols
+ * (cols padded to a multiple of 32). */
 int64_t mxo_packed_bytes(int fmt, int64_t rows, int64_t cols);
 
 /* Whole-tensor quantize.  x is [rows x cols] with leading dimension ld (in
- * elements), fp32 or bf16 bit patterns.  Row-wise outputs: q_row [rows x cols]
- * packed, s_row [rows x cols/32].  Column-wise outputs are stored transposed:
- * q_colt [cols x rows] packed, s_colt [cols x rows/32].  Returns 0 on success,
- * -1 on a bad argument. */
+ * elements), fp32 or bf16 bit patterns.  With R_p, C_p the dimensions padded
+ * to multiples of 32: row-wise outputs q_row [rows x C_p] packed, s_row
+ * [rows x C_p/32]; column-wise outputs stored transposed, q_colt [cols x R_p]
+ * packed, s_colt [cols x R_p/32].  Returns 0 on success, -1 on a bad
+ * argument. */
 int mxo_quantize(int src, const void* x, int64_t rows, int64_t cols, int64_t ld,
                  int fmt, unsigned layouts, int round, unsigned flags,
                  uint64_t seed, uint64_t counter_offset, uint32_t hadamard_signs,
                  uint8_t* q_row, uint8_t* s_row, uint8_t* q_colt, uint8_t* s_colt);
 
-/* Dequantize a packed [rows x cols] tensor whose blocks run along cols to fp32. */
+/* Dequantize a packed [rows x C_p] tensor whose blocks run along cols to fp32
+ * y [rows x cols] (the padded positions are dropped). */
 int mxo_dequantize(const uint8_t* q, const uint8_t* s, int fmt, int64_t rows, int64_t cols,
                    float* y);
 
 /* C[m,n] = sum_k a[m,k] * b[n,k] over the dequantized operands, in fp64, with
  * T[m,n] = sum_k |a[m,k] * b[n,k]|.  A is [M x K], B is given as B^T [N x K];
- * both have their blocks along K.  t may be NULL. */
+ * both have their blocks along K, and k runs over K padded to a multiple of
+ * 32 (the padded positions are part of the operands).  t may be NULL. */
 int mxo_gemm_f64(const uint8_t* a_q, const uint8_t* a_s, int a_fmt,
                  const uint8_t* b_q, const uint8_t* b_s, int b_fmt,
                  int64_t M, int64_t N, int64_t K, double* c, double* t);
