@@ -23,9 +23,10 @@
  *
  * Conventions for every entry point:
  *   - All data pointers are DEVICE pointers, owned by the caller.  The library
- *     never allocates or frees memory; its only global state is a kernel
- *     attribute (the general GEMM kernels' LDS size) set once on first use,
- *     idempotently, so calls are thread-safe.
+ *     never allocates or frees memory.  Its only global state is the compute-
+ *     unit count of each device (which sizes the GEMM's persistent grid),
+ *     looked up on first use and kept in a relaxed atomic per device: calls
+ *     are thread-safe.  Calls run on the current HIP device.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *     default stream).  Device faults surface at the caller's next
  *     synchronization on that stream.
@@ -39,11 +40,14 @@
  *     32-element block, element j in bits 6j..6j+5 of the little-endian 192-bit
  *     block; FP4 (E2M1) two per byte, even element in the low nibble.
  *   - scales: one E8M0 byte per block, in a separate array.
+ *   - partial blocks: a blocked dimension n that is not a multiple of 32 is
+ *     stored as if the source were padded with zeros to n_p = 32 * ceil(n/32);
+ *     the padded elements of the last block are part of the packed output.
  *   - row-wise layout: blocks run along the columns of the [rows x cols] source;
- *     q_row is [rows x cols] packed (row pitch mx_packed_bytes(fmt, 1, cols)),
- *     s_row is [rows x cols/32].
+ *     q_row is [rows x cols_p] packed (row pitch mx_packed_bytes(fmt, 1, cols)),
+ *     s_row is [rows x cols_p/32].
  *   - column-wise layout, stored transposed: blocks run along the rows of the
- *     source; q_colt is [cols x rows] packed, s_colt is [cols x rows/32].
+ *     source; q_colt is [cols x rows_p] packed, s_colt is [cols x rows_p/32].
  */
 #ifndef MX_H
 #define MX_H
@@ -60,7 +64,7 @@ typedef struct ihipStream_t* mx_stream_t;
 typedef enum {
   MX_OK = 0,
   MX_ERR_ARG = -1,         /* bad enum value, null pointer or negative size */
-  MX_ERR_SHAPE = -2,       /* a blocked dimension is not a multiple of 32, ld too small */
+  MX_ERR_SHAPE = -2,       /* leading dimension smaller than the row          */
   MX_ERR_ALIGN = -3,       /* pointer or leading dimension breaks the 16-byte rule */
   MX_ERR_UNSUPPORTED = -4, /* valid request this build does not implement */
   MX_ERR_HIP = -5          /* the HIP runtime refused a launch */
@@ -95,7 +99,8 @@ typedef struct {
  *   q_row, s_row    outputs of the row-wise layout (required iff requested).
  *   q_colt, s_colt  outputs of the column-wise layout, transposed (required iff
  *                   requested).  Packed outputs must be 16-byte aligned.
- * Shapes: cols % 32 == 0 always; rows % 32 == 0 when MX_LAYOUT_COLT is asked.
+ * Shapes: any rows, cols >= 0; a short last block along the block axis reads
+ * the missing elements as +0 (the source is never read past cols).
  *
  * Per block: subnormal fp32 values become signed zero; with MX_FLAG_HADAMARD32
  * the 32 values (along the block axis) are sign-flipped per hadamard_signs,
@@ -107,8 +112,10 @@ typedef struct {
  * r < floor(frac * 2^32) (MX_SR) with r the element's Philox4x32-10 word: key =
  * seed, counter = (j lo, j hi, layout, 0) with j = counter_offset + (i >> 2),
  * i = row * cols + col its source index, word i & 3, layout 0 row-wise and 1
- * column-wise.  Results saturate at the largest normal; zeros keep their sign
- * except in INT8, whose elements are n/64 with n in [-127, 127].
+ * column-wise; with a short last block, i is the index in the zero-padded
+ * source, row * cols_p + col.  Results saturate at the largest normal; zeros
+ * keep their sign except in INT8, whose elements are n/64 with n in
+ * [-127, 127].
  */
 int mx_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, const mx_quant_params* p,
                 void* q_row, uint8_t* s_row, void* q_colt, uint8_t* s_colt, mx_stream_t stream);
@@ -118,8 +125,9 @@ int mx_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, const m
  * run along cols (section 2 of the MX summary).  A NaN scale (0xFF) gives a NaN
  * block; element NaN / Inf codes decode to NaN / Inf; products beyond fp32
  * overflow to Inf; fp32 subnormal results are kept.
- *   q  packed elements, 16-byte aligned;  s  [rows x cols/32] scales;
- *   y  [rows x cols] fp32 output, 16-byte aligned.  cols % 32 == 0.
+ *   q  packed elements [rows x cols_p], 16-byte aligned;  s  [rows x cols_p/32]
+ *      scales (cols_p: cols padded to a multiple of 32);
+ *   y  [rows x cols] fp32 output, 16-byte aligned (the padding is dropped).
  */
 int mx_dequantize(const void* q, const uint8_t* s, int32_t fmt, int64_t rows, int64_t cols,
                   float* y, mx_stream_t stream);
@@ -136,8 +144,15 @@ int mx_dequantize(const void* q, const uint8_t* s, int32_t fmt, int64_t rows, in
  * Formats: E4M3, E5M2, E2M3, E3M2, E2M1 for either operand (any mix), or
  * MX_INT8 for both (INT8 mixed with another format returns
  * MX_ERR_UNSUPPORTED).  MXINT8 products are formed exactly (each element times
- * its scale is exact in bf16 wherever it is a normal number) and summed in
- * fp32.  K % 32 == 0; operand pointers 16-byte aligned.
+ * its scale is exact in bf16, subnormals included) and summed in fp32.  Any
+ * K >= 0: with K % 32 != 0 the operands hold K_p = 32 * ceil(K/32) elements
+ * per row (the zero-padded last block mx_quantize writes) and the sums run
+ * over all K_p.  Operand pointers 16-byte aligned.
+ * Accuracy: |C - C_exact| <= 1e-5 * sum|a * b| on every tested workload with
+ * K >= 512.  For FP8 and E3M2 operands the block-scaled instruction truncates
+ * products within groups of 8 along K, so a product dominated by one or a few
+ * blocks (short K, or block scales spread by 2^60) can exceed that bound by a
+ * small factor; E2M1, E2M3 and MXINT8 products are exact.
  * The result of a block whose scale is 0xFF is unspecified (the hardware's
  * NaN-scale behaviour); no configuration here produces such scales from finite
  * inputs.
@@ -169,19 +184,22 @@ int mx_gemm_bf16(const void* a_q, const uint8_t* a_s, int32_t a_fmt, const void*
  * computes; the fp32 C itself is never written.
  *   a_q .. K   as for mx_gemm.
  *   c_fmt      MX_E4M3, MX_E5M2 or MX_E2M1 (others: MX_ERR_UNSUPPORTED).
- *   c_q        [M x N] packed codes, row pitch N * bits / 8, 16-byte aligned.
- *   c_s        [M x N/32] scales.
- * N % 32 == 0 and K % 32 == 0 (MX_ERR_SHAPE).  The fused epilogue lives in
- * the staged MFMA kernel only: it needs K a positive multiple of 512, 16-byte aligned scale
- * arrays and operands under 4 GiB; outside that the call returns
- * MX_ERR_UNSUPPORTED and writes nothing.  M == 0 or N == 0 writes nothing.
+ *   c_q        [M x N_p] packed codes, row pitch mx_packed_bytes(c_fmt, 1, N),
+ *              16-byte aligned (N_p: N padded to a multiple of 32; a short last
+ *              block holds zeros past N).
+ *   c_s        [M x N_p/32] scales.
+ * The fused epilogue lives in the staged MFMA kernel only: it needs K_p a
+ * positive multiple of 512, 16-byte aligned scale arrays and operands under
+ * 4 GiB; outside that the call returns MX_ERR_UNSUPPORTED and writes nothing.
+ * M == 0 or N == 0 writes nothing.
  */
 int mx_gemm_mx(const void* a_q, const uint8_t* a_s, int32_t a_fmt, const void* b_q,
                const uint8_t* b_s, int32_t b_fmt, int64_t M, int64_t N, int64_t K,
                int32_t c_fmt, void* c_q, uint8_t* c_s, mx_stream_t stream);
 
 /* Host-only helpers: bytes of a packed [rows x cols] element array (blocks
- * along cols) and of its scale array; -1 on a bad argument. */
+ * along cols, a short last block padded to 32 elements) and of its scale
+ * array; -1 on a bad argument. */
 int64_t mx_packed_bytes(int32_t fmt, int64_t rows, int64_t cols);
 int64_t mx_scale_bytes(int64_t rows, int64_t cols);
 /* Static description of a status code. */

@@ -15,18 +15,21 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
 
+// blocks of a dimension of n elements (a short last block is padded)
+int64_t blocks(int64_t n) { return (n + 31) / 32; }
+
 }  // namespace
 
 extern "C" {
 
 int64_t mx_packed_bytes(int32_t fmt, int64_t rows, int64_t cols) {
-  if (!fmt_ok(fmt) || rows < 0 || cols < 0 || cols % 32) return -1;
-  return rows * (cols / 32) * (4 * mx::elem_bits(fmt));
+  if (!fmt_ok(fmt) || rows < 0 || cols < 0) return -1;
+  return rows * blocks(cols) * (4 * mx::elem_bits(fmt));
 }
 
 int64_t mx_scale_bytes(int64_t rows, int64_t cols) {
-  if (rows < 0 || cols < 0 || cols % 32) return -1;
-  return rows * (cols / 32);
+  if (rows < 0 || cols < 0) return -1;
+  return rows * blocks(cols);
 }
 
 const char* mx_status_str(int status) {
@@ -54,8 +57,6 @@ int mx_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, const m
   if (p->flags & ~(uint32_t)MX_FLAG_HADAMARD32) return MX_ERR_ARG;
   if (rows < 0 || cols < 0) return MX_ERR_ARG;
   if (ld_x < cols) return MX_ERR_SHAPE;
-  if (cols % 32) return MX_ERR_SHAPE;
-  if ((lay & MX_LAYOUT_COLT) && rows % 32) return MX_ERR_SHAPE;
   const bool do_row = lay & MX_LAYOUT_ROW, do_col = lay & MX_LAYOUT_COLT;
   if (rows == 0 || cols == 0) return MX_OK;
   if (do_row && (!q_row || !s_row)) return MX_ERR_ARG;
@@ -90,7 +91,6 @@ int mx_dequantize(const void* q, const uint8_t* s, int32_t fmt, int64_t rows, in
                   float* y, mx_stream_t stream) {
   if (!fmt_ok(fmt)) return MX_ERR_ARG;
   if (rows < 0 || cols < 0) return MX_ERR_ARG;
-  if (cols % 32) return MX_ERR_SHAPE;
   if (rows == 0 || cols == 0) return MX_OK;
   if (!q || !s || !y) return MX_ERR_ARG;
   if (!aligned16(q) || !aligned16(y)) return MX_ERR_ALIGN;
@@ -103,14 +103,13 @@ int mx_gemm(const void* a_q, const uint8_t* a_s, int32_t a_fmt, const void* b_q,
   if (!fmt_ok(a_fmt) || !fmt_ok(b_fmt)) return MX_ERR_ARG;
   if ((a_fmt == MX_INT8) != (b_fmt == MX_INT8)) return MX_ERR_UNSUPPORTED;
   if (M < 0 || N < 0 || K < 0) return MX_ERR_ARG;
-  if (K % 32) return MX_ERR_SHAPE;
   if (ldc < N) return MX_ERR_SHAPE;
   if (M == 0 || N == 0) return MX_OK;
   if (!c) return MX_ERR_ARG;
   if (K > 0 && (!a_q || !a_s || !b_q || !b_s)) return MX_ERR_ARG;
   if (K > 0 && (!aligned16(a_q) || !aligned16(b_q))) return MX_ERR_ALIGN;
-  return hip_status(mx::launch_gemm(a_q, a_s, a_fmt, b_q, b_s, b_fmt, M, N, K, c, ldc, -1, nullptr,
-                                    nullptr, (hipStream_t)stream));
+  return hip_status(mx::launch_gemm(a_q, a_s, a_fmt, b_q, b_s, b_fmt, M, N, 32 * blocks(K), c, ldc,
+                                    -1, nullptr, nullptr, (hipStream_t)stream));
 }
 
 int mx_gemm_bf16(const void* a_q, const uint8_t* a_s, int32_t a_fmt, const void* b_q,
@@ -119,15 +118,15 @@ int mx_gemm_bf16(const void* a_q, const uint8_t* a_s, int32_t a_fmt, const void*
   if (!fmt_ok(a_fmt) || !fmt_ok(b_fmt)) return MX_ERR_ARG;
   if ((a_fmt == MX_INT8) != (b_fmt == MX_INT8)) return MX_ERR_UNSUPPORTED;
   if (M < 0 || N < 0 || K < 0) return MX_ERR_ARG;
-  if (K % 32) return MX_ERR_SHAPE;
   if (ldc < N) return MX_ERR_SHAPE;
   if (M == 0 || N == 0) return MX_OK;
   if (!c) return MX_ERR_ARG;
   if (K > 0 && (!a_q || !a_s || !b_q || !b_s)) return MX_ERR_ARG;
   if (K > 0 && (!aligned16(a_q) || !aligned16(b_q))) return MX_ERR_ALIGN;
   if ((uintptr_t)c % 2) return MX_ERR_ALIGN;
-  return hip_status(mx::launch_gemm(a_q, a_s, a_fmt, b_q, b_s, b_fmt, M, N, K, nullptr, ldc,
-                                    mx::GEMM_OUT_BF16, (uint8_t*)c, nullptr, (hipStream_t)stream));
+  return hip_status(mx::launch_gemm(a_q, a_s, a_fmt, b_q, b_s, b_fmt, M, N, 32 * blocks(K), nullptr,
+                                    ldc, mx::GEMM_OUT_BF16, (uint8_t*)c, nullptr,
+                                    (hipStream_t)stream));
 }
 
 int mx_gemm_mx(const void* a_q, const uint8_t* a_s, int32_t a_fmt, const void* b_q,
@@ -137,13 +136,12 @@ int mx_gemm_mx(const void* a_q, const uint8_t* a_s, int32_t a_fmt, const void* b
   if (a_fmt == MX_INT8 || b_fmt == MX_INT8) return MX_ERR_UNSUPPORTED;
   if (c_fmt != MX_E4M3 && c_fmt != MX_E5M2 && c_fmt != MX_E2M1) return MX_ERR_UNSUPPORTED;
   if (M < 0 || N < 0 || K < 0) return MX_ERR_ARG;
-  if (K % 32 || N % 32) return MX_ERR_SHAPE;
   if (M == 0 || N == 0) return MX_OK;
   if (!c_q || !c_s) return MX_ERR_ARG;
   if (!a_q || !a_s || !b_q || !b_s) return MX_ERR_ARG;
   if (!aligned16(a_q) || !aligned16(b_q) || !aligned16(c_q)) return MX_ERR_ALIGN;
-  const hipError_t e = mx::launch_gemm(a_q, a_s, a_fmt, b_q, b_s, b_fmt, M, N, K, nullptr, N, c_fmt,
-                                       (uint8_t*)c_q, c_s, (hipStream_t)stream);
+  const hipError_t e = mx::launch_gemm(a_q, a_s, a_fmt, b_q, b_s, b_fmt, M, N, 32 * blocks(K),
+                                       nullptr, N, c_fmt, (uint8_t*)c_q, c_s, (hipStream_t)stream);
   return e == hipErrorNotSupported ? MX_ERR_UNSUPPORTED : hip_status(e);
 }
 

@@ -56,16 +56,20 @@ __device__ __forceinline__ void unpack8(const uint8_t* row, int64_t c, uint32_t 
   }
 }
 
+// q holds rows of cols padded to whole blocks (cp elements); y is [rows x cols]
+// and the padded positions are dropped.
 template <int F>
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ q,
                                                  const uint8_t* __restrict__ s, int64_t rows,
                                                  int64_t cols, float* __restrict__ y) {
-  const int64_t cpr = cols >> 3;
+  const int64_t cp = (cols + 31) / 32 * 32;
+  const int64_t cpr = (cols + 7) >> 3;  // chunks of 8 holding at least one element
   const int64_t n = rows * cpr;
-  const int64_t pitch = cols * Fmt<F>::bits / 8;
+  const int64_t pitch = cp * Fmt<F>::bits / 8;
+  const bool vec = (cols & 3) == 0;     // rows of y start 16-byte aligned
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     const int64_t r = i / cpr, c = i - r * cpr;
-    const uint32_t sc = s[r * (cols >> 5) + (c >> 2)];
+    const uint32_t sc = s[r * (cp >> 5) + (c >> 2)];
     uint32_t codes[8];
     unpack8<F>(q + r * pitch, c, codes);
     float o[8];
@@ -74,15 +78,22 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ q,
       const float v = decode<F>(codes[k]);
       o[k] = sc == 0xFFu ? __builtin_nanf("") : __builtin_amdgcn_ldexpf(v, (int)sc - 127);
     }
-    float4* dst = (float4*)(y + r * cols + 8 * c);
-    dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-    dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+    float* yr = y + r * cols + 8 * c;
+    if (vec && 8 * c + 8 <= cols) {
+      float4* dst = (float4*)yr;
+      dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; k++)
+        if (8 * c + k < cols) yr[k] = o[k];
+    }
   }
 }
 
 hipError_t launch_dequant(const void* q, const uint8_t* s, int fmt, int64_t rows, int64_t cols,
                           float* y, hipStream_t st) {
-  const int64_t n = rows * (cols / 8);
+  const int64_t n = rows * ((cols + 7) / 8);
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   const dim3 g((unsigned)blocks), b(256);

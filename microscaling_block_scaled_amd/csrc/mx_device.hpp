@@ -162,6 +162,9 @@ __device__ __forceinline__ v4i make_rsrc(const void* p, uint32_t bytes) {
 // instruction has no register result.  A load that takes its LDS address
 // from M0 needs one wait state after the write of M0.
 __device__ __forceinline__ void dma16(v4i rs, uint32_t voff, uint32_t soff, uint32_t lds_dst) {
+  // a constant offset stays in a scalar register (the instruction takes no
+  // literal there)
+  asm("" : "+s"(soff));
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
                :
                : "v"(voff), "s"(rs), "s"(lds_dst), "s"(soff)

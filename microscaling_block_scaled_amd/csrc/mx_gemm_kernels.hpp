@@ -1,18 +1,20 @@
-// mx_gemm.hip -- block-scaled MX matrix multiply on gfx950's
-// V_MFMA_SCALE_F32_16X16X128_F8F6F4.
+// mx_gemm_kernels.hpp -- block-scaled MX matrix multiply on gfx950's
+// V_MFMA_SCALE_F32_{16X16X128,32X32X64}_F8F6F4 (kernel templates; the build
+// compiles one unit per operand-format pair that instantiates gemm_launch,
+// and mx_gemm.hip dispatches to them).
 //
 // C[m,n] = sum over 32-element blocks kb of 2^(sa[m,kb]-127) * 2^(sb[n,kb]-127)
 //          * sum_{k in kb} P_A[m,k] * P_B[n,k]
 // ("Microscaling Data Formats for Deep Learning", summary section 4: dot
 // products consume MX operands and return scalar floats; section 2: v = X * P).
 // The E8M0 scales are applied inside the matrix instruction, accumulation is
-// fp32 and C is fp32.
+// fp32 and C is fp32 (or bf16, or MX).
 //
-// Tiling: a 256-thread workgroup computes a 256 x 256 tile of C; its four
-// waves each own 128 x 128 (8 x 8 instructions of 16 x 16 x 128).  Per K-step
-// of 128 elements the A and B panels (256 rows each, with their scale bytes)
-// are copied global -> registers -> LDS, double buffered, so the copy of step
-// s+1 overlaps the instructions of step s.
+// General kernel (k_gemm; any K % 32 == 0): a 256-thread workgroup computes a
+// 256 x 256 tile of C; its four waves each own 128 x 128 (8 x 8 instructions
+// of 16 x 16 x 128).  Per K-step of 128 elements the A and B panels (256 rows
+// each, with their scale bytes) are copied global -> registers -> LDS, double
+// buffered, so the copy of step s+1 overlaps the instructions of step s.
 //
 // Operand lane layouts of the 16x16x128 instruction (lane l, row l % 16, block
 // kb = l / 16 of the K-step; the scale operand of lane l is the E8M0 byte of
@@ -22,6 +24,9 @@
 //   FP6 (E2M3, E3M2): the 24 packed bytes of block kb
 //   FP4 (E2M1):       the 16 packed bytes of block kb
 // Result: lane l holds C rows 4 (l / 16) + v, v = 0..3, column l % 16.
+#pragma once
+
+#include <atomic>
 #include <utility>
 
 #include "mx_convert.hpp"
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ aq,
                                               int64_t N, int64_t K, float* __restrict__ c,
                                               uint16_t* __restrict__ cb, int64_t ldc, int tiles_n) {
   using L = GemmLds<FA, FB>;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[L::TOTAL];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
@@ -269,6 +274,8 @@ __device__ __forceinline__ v8bf i8_bf16(uint2 w, int s) {
 // K-steps of four blocks through two LDS stages); per block one 16x16x32 bf16
 // instruction per 16 x 16 output tile.  Lane l supplies row l % 16 of its
 // operand tile, elements 8 (l / 16) .. 8 (l / 16) + 7 of the block.
+// (a template only so that the units of other formats do not compile it)
+template <int I8 = INT8>
 __global__ __launch_bounds__(256) void k_gemm_i8(const uint8_t* __restrict__ aq,
                                                  const uint8_t* __restrict__ as,
                                                  const uint8_t* __restrict__ bq,
@@ -278,7 +285,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(const uint8_t* __restrict__ aq,
                                                  int tiles_n) {
   using L = GemmLds<INT8, INT8>;
   using O = Op<INT8>;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[L::TOTAL];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
@@ -355,38 +362,38 @@ __global__ __launch_bounds__(256) void k_gemm_i8(const uint8_t* __restrict__ aq,
   }
 }
 
+template <int I8 = INT8>
 static hipError_t gemm_i8_launch(const void* aq, const uint8_t* as, const void* bq,
                                  const uint8_t* bs, int64_t M, int64_t N, int64_t K, float* c,
                                  int64_t ldc, int out_fmt, uint8_t* out_q, hipStream_t st) {
   if (out_fmt >= 0 && out_fmt != GEMM_OUT_BF16) return hipErrorNotSupported;
-  using L = GemmLds<INT8, INT8>;
   const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  static bool attr_done = false;  // benign race: the call is idempotent
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_i8,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
-  hipLaunchKernelGGL(k_gemm_i8, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), L::TOTAL, st,
+  hipLaunchKernelGGL(k_gemm_i8<I8>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st,
                      (const uint8_t*)aq, as, (const uint8_t*)bq, bs, M, N, K, c,
                      out_fmt == GEMM_OUT_BF16 ? (uint16_t*)out_q : nullptr, ldc, (int)tiles_n);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// fast path (K % 512 == 0, scale arrays 16-byte aligned, operands < 4 GiB)
+// staged kernel (K % 512 == 0, scale arrays 16-byte aligned, operands < 4 GiB)
 //
-// A 256-thread workgroup computes a 256 x 256 tile of C.  Per stage of KS
-// elements of K (256 when both operands are FP4, so that every operand row of
-// a stage is one 128-byte line; else 128) the A and B panels (256 rows each)
-// go global -> LDS directly (buffer_load ... lds; rows past the matrix edge
-// fall outside the buffer and read zero) into a ring of NST stages, issued
-// NST - 1 stages ahead.  Panel rows are stored unpadded with their 16-byte
-// chunks XOR-swizzled so that the rows read at one K offset hit distinct LDS
-// banks.  The E8M0 scales travel separately, 32 bytes (1024 elements of K) per
-// row at a time, into two alternating LDS buffers: one 16-byte load per lane
-// pair and row instead of a few bytes per row and stage.
+// Persistent: the grid holds one workgroup per compute unit (at most one fits:
+// it takes the whole LDS and all registers of its SIMDs), and workgroup b
+// computes the 256 x 256 tiles b, b + G, b + 2G, ... of C (G workgroups).  Per
+// stage of KS elements of K (256 when both operands are FP4, so that every
+// operand row of a stage is one 128-byte line; else 128) the A and B panels
+// (256 rows each) go global -> LDS directly (buffer_load ... lds; rows past the
+// matrix edge fall outside the buffer and read zero) into a ring of NST
+// stages, issued NST - 1 stages ahead.  The stages of a workgroup's tiles form
+// one stream: the last stages of a tile load the first stages of its next
+// tile, so the ring never drains between tiles.  Panel rows are stored
+// unpadded with their 16-byte chunks XOR-swizzled so that the rows read at one
+// K offset hit distinct LDS banks.  The E8M0 scales travel separately, 32
+// bytes (1024 elements of K) per row at a time, into two alternating LDS
+// buffers: one 16-byte load per lane pair and row instead of a few bytes per
+// row and stage.  Every offset that can reach past a matrix (rows past M or N,
+// the last scale chunk of a row) is in the range-checked VGPR offset of its
+// load, relative to a buffer resource that starts at the tile.
 //
 // Four waves own 128 x 128 pieces of the tile, with their accumulators in the
 // AGPR file.  A stage is SUB substeps of 64 elements of K (one
@@ -396,6 +403,13 @@ static hipError_t gemm_i8_launch(const void* aq, const uint8_t* as, const void* 
 // while those operands arrive.  One barrier per stage, as soon as the stage's
 // operands are all read, hands the ring slot back to the loads, which are
 // then spread over the rest of the stage.
+//
+// The first substep of a tile starts its sums from zero (the instruction's
+// accumulator operand is the constant 0) and, for fp32 and bf16 output, stores
+// the previous tile's results piece by piece just before each instruction
+// overwrites them, so C leaves while the matrix unit works on the next tile.
+// The output kind is a template parameter: each instantiation carries one
+// epilogue.
 // ---------------------------------------------------------------------------
 typedef float v16f __attribute__((ext_vector_type(16)));
 
@@ -522,15 +536,16 @@ struct Lanes {
 };
 
 // The scale bytes of one stage for the wave's 8 tiles: KS / 32 bytes per row
-// (one or two dwords), read once per stage.
+// (one or two dwords), read once per stage from chunk buffer `par` at byte
+// offset `off` of each row's 32.
 template <int KS> struct ScaleWords {
   uint32_t a[4][KS / 128], b[4][KS / 128];
 };
 
-template <class C, int FA, int FB>
-__device__ __forceinline__ void read_scale_words(ScaleWords<C::KS>& sw, const uint8_t* lds, int s,
-                                                 const Lanes& w) {
-  const uint8_t* sc = lds + C::SC_OFF + ((s / C::SPC) & 1) * C::SC_BUF + (s % C::SPC) * (C::KS / 32);
+template <class C>
+__device__ __forceinline__ void read_scale_words(ScaleWords<C::KS>& sw, const uint8_t* lds, int par,
+                                                 int off, const Lanes& w) {
+  const uint8_t* sc = lds + C::SC_OFF + par * C::SC_BUF + off;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const uint8_t* pa = sc + (w.arow + 32 * i) * C::SC_ROW;
@@ -583,15 +598,19 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// One substep: the 16 block-scaled instructions on `cur`, each followed by
-// `slot(k)` (LDS reads of the next substep's operands, the barrier, loads),
-// in exactly this order (scheduling fences).  B is the instruction's first
-// operand, so a lane's results are four consecutive columns of C.
-template <int FA, int FB, class Slot>
-__device__ __forceinline__ void substep(v16f (&acc)[4][4], const Ops& cur, Slot&& slot) {
+// One substep: the 16 block-scaled instructions on `cur`, each preceded by
+// `pre(k)` and followed by `slot(k)` (LDS reads of the next substep's
+// operands, the barrier, loads), in exactly this order (scheduling fences).
+// With ZERO the instructions start from zero instead of adding to acc.  B is
+// the instruction's first operand, so a lane's results are four consecutive
+// columns of C.
+template <int FA, int FB, bool ZERO, class Pre, class Slot>
+__device__ __forceinline__ void substep(v16f (&acc)[4][4], const Ops& cur, Pre&& pre, Slot&& slot) {
   static_for<16>([&](auto K) {
     constexpr int k = decltype(K)::value, i = k >> 2, j = k & 3;
-    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.b[j], cur.a[i], acc[i][j], FB, FA,
+    pre(K);
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.b[j], cur.a[i],
+                                                                ZERO ? v16f{} : acc[i][j], FB, FA,
                                                                 0, cur.sb[j], 0, cur.sa[i]);
     slot(K);
     __builtin_amdgcn_sched_barrier(0);
@@ -604,10 +623,11 @@ __device__ __forceinline__ void substep(v16f (&acc)[4][4], const Ops& cur, Slot&
 // in (i8_bf16) and feed 16 bf16 32x32x16 instructions.  A and B lanes take
 // the same K positions in the same slice, so the four slices together cover
 // the substep's 64 products of every (row, column) pair exactly once, in a
-// different order from the block-scaled instruction.  slot(k) follows every
-// fourth instruction, in order.
-template <class Slot>
-__device__ __forceinline__ void substep_i8(v16f (&acc)[4][4], const Ops& cur, Slot&& slot) {
+// different order from the block-scaled instruction.  pre(k) precedes the
+// first slice's instruction k; slot(k) follows every fourth instruction, in
+// order.  With ZERO the first slice starts from zero.
+template <bool ZERO, class Pre, class Slot>
+__device__ __forceinline__ void substep_i8(v16f (&acc)[4][4], const Ops& cur, Pre&& pre, Slot&& slot) {
   auto convert = [&](int t, v8bf (&a8)[4], v8bf (&b8)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -626,7 +646,9 @@ __device__ __forceinline__ void substep_i8(v16f (&acc)[4][4], const Ops& cur, Sl
     static_for<16>([&](auto K) {
       constexpr int k = decltype(K)::value, i = k >> 2, j = k & 3;
       if constexpr (k == 12 && t < 3) convert(t + 1, a8[c ^ 1], b8[c ^ 1]);
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b8[c][j], a8[c][i], acc[i][j], 0, 0, 0);
+      if constexpr (t == 0) pre(K);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b8[c][j], a8[c][i],
+                                                          ZERO && t == 0 ? v16f{} : acc[i][j], 0, 0, 0);
       if constexpr (k % 4 == 3) slot(std::integral_constant<int, 4 * t + k / 4>{});
     });
   });
@@ -652,9 +674,9 @@ __device__ __forceinline__ void acc_settle() { asm volatile("s_nop 7\n\ts_nop 7\
 // product, round to nearest even), as "Format-Aware Fusion for Fast FP4
 // Pretraining" fuses the quantization into the producer.
 struct MxOut {
-  int fmt;         // E4M3, E5M2 or E2M1; GEMM_OUT_BF16: bf16 C at q; negative: fp32 C
-  uint8_t* q;      // [M x N] packed codes, row pitch N * bits / 8
-  uint8_t* s;      // [M x N/32] scales
+  int fmt;         // E4M3, E5M2 or E2M1
+  uint8_t* q;      // [M x N_p] packed codes (N_p: N padded to whole blocks)
+  uint8_t* s;      // [M x N_p/32] scales
 };
 
 // A wave's 128 x 128 piece (rows r0.., columns c0.., c0 % 128 == 0) as MX
@@ -673,7 +695,7 @@ __device__ __forceinline__ void store_mx(const v16f (&acc)[4][4], const MxOut& m
   constexpr int bits = Fmt<F>::bits;
   const int lr = lane & 31, hi = lane >> 5;
   const int partner = (lane ^ 32) << 2;
-  const int64_t nb = N >> 5;
+  const int64_t nb = (N + 31) >> 5;  // blocks per row; a short last block is padded
   const int64_t blk0 = c0 >> 5;
   const bool s_dword = (nb & 3) == 0 && ((uintptr_t)mo.s & 3) == 0 && blk0 + 3 < nb;
   acc_settle();
@@ -751,7 +773,7 @@ __device__ __forceinline__ void store_mx(const v16f (&acc)[4][4], const MxOut& m
         const uint32_t g2 = p[j][1].w[0], g3 = p[j][1].w[1];
         const uint32_t r1 = x[j][0], r2 = x[j][1];
         const uint4 o = hi ? make_uint4(r1, g2, r2, g3) : make_uint4(g0, r1, g1, r2);
-        if (live) *(uint4*)(mo.q + row * N + 32 * blk + 16 * hi) = o;
+        if (live) *(uint4*)(mo.q + row * (32 * nb) + 32 * blk + 16 * hi) = o;
       } else {
         const uint32_t r = x[j][0];
         const uint32_t own = hi ? p[j][1].w[0] : p[j][0].w[0];
@@ -763,7 +785,7 @@ __device__ __forceinline__ void store_mx(const v16f (&acc)[4][4], const MxOut& m
           o.x = (own & 0xFFFFu) | (r << 16);
           o.y = (own >> 16) | (r & 0xFFFF0000u);
         }
-        if (live) *(uint2*)(mo.q + row * (N >> 1) + 16 * blk + 8 * hi) = o;
+        if (live) *(uint2*)(mo.q + row * (16 * nb) + 16 * blk + 8 * hi) = o;
       }
     }
     // scales: both lanes of a row hold its four codes; the low lane stores
@@ -781,18 +803,72 @@ __device__ __forceinline__ void store_mx(const v16f (&acc)[4][4], const MxOut& m
   }
 }
 
-template <int FA, int FB, int KS>
-__global__ __launch_bounds__(256) void k_gemm_fast(const uint8_t* __restrict__ aq,
-                                                   const uint8_t* __restrict__ as,
-                                                   const uint8_t* __restrict__ bq,
-                                                   const uint8_t* __restrict__ bs, int64_t M,
-                                                   int64_t N, int64_t K, float* __restrict__ c,
-                                                   int64_t ldc, int tiles_m, int tiles_n,
-                                                   int vec_store, MxOut mo) {
+// Output kinds of the staged kernel.
+enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_MX_E4M3 = 2, OUT_MX_E5M2 = 3, OUT_MX_E2M1 = 4 };
+template <int OUT> struct OutMx { static constexpr int fmt = OUT == OUT_MX_E4M3 ? E4M3 : (OUT == OUT_MX_E5M2 ? E5M2 : E2M1); };
+
+struct FastArgs {
+  const uint8_t* aq;
+  const uint8_t* as;
+  const uint8_t* bq;
+  const uint8_t* bs;
+  int64_t M, N, K;
+  void* c;        // fp32 C, bf16 C, or MX codes
+  uint8_t* cs;    // MX scales
+  int64_t ldc;    // fp32 / bf16 C: row pitch in elements
+  int tiles_m, tiles_n;
+  int vec;        // fp32 / bf16 C: 16 / 8-byte stores allowed (pointer and pitch aligned)
+};
+
+// Stores of one 32 x 32 accumulator tile acc[i][j] of a wave's 128 x 128 piece
+// (rows r0 + 32 i + l % 32, columns c0 + 32 j + 8 q + 4 (l / 32) + e for
+// element 4 q + e of lane l), fp32 or bf16, inside M x N.  With ASM the bf16
+// values are read one accumulator at a time (acc_bits), which keeps the
+// conversion's registers few while the operand ring is live; the tile must
+// then not have been written by one of the last few matrix instructions.
+template <int OUT, bool ASM = false>
+__device__ __forceinline__ void store_tile(const v16f& t, const FastArgs& g, int64_t r0, int64_t c0,
+                                           int i, int j, int lane) {
+  auto val = [&](int k) {
+    if constexpr (ASM) return __builtin_bit_cast(float, acc_bits(t, k));
+    else return t[k];
+  };
+  const int64_t row = r0 + 32 * i + (lane & 31);
+  if (row >= g.M) return;
+  const int64_t col0 = c0 + 32 * j + 4 * (lane >> 5);
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const int64_t col = col0 + 8 * q;
+    if (OUT == OUT_F32) {
+      float* crow = (float*)g.c + row * g.ldc;
+      if (g.vec && col + 3 < g.N) {
+        *(float4*)(crow + col) = make_float4(t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+          if (col + e < g.N) crow[col + e] = t[4 * q + e];
+      }
+    } else {
+      uint16_t* crow = (uint16_t*)g.c + row * g.ldc;
+      if (g.vec && col + 3 < g.N) {
+        *(uint2*)(crow + col) = make_uint2(bf16x2_bits(val(4 * q), val(4 * q + 1)),
+                                           bf16x2_bits(val(4 * q + 2), val(4 * q + 3)));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+          if (col + e < g.N) crow[col + e] = bf16_bits(val(4 * q + e));
+      }
+    }
+  }
+}
+
+template <int FA, int FB, int KS, int OUT>
+__global__ __launch_bounds__(256) void k_gemm_fast(FastArgs g) {
   using C = Fast<FA, FB, KS>;
   constexpr int NST = C::NST, SUB = C::SUB, SPC = C::SPC;
   constexpr int SEGS = C::CHA + C::CHB;  // 1 KB panel segments per wave per stage
   constexpr int SEG_A = 4 * C::CHA;
+  constexpr bool MXO = OUT >= OUT_MX_E4M3;
   // An accumulation-register operand anywhere in the kernel lets the compiler
   // place the accumulators in the AGPR file (256 of them per wave), leaving
   // the VGPRs to two substeps of operands.
@@ -802,17 +878,17 @@ __global__ __launch_bounds__(256) void k_gemm_fast(const uint8_t* __restrict__ a
   // wave index as a wave-uniform (scalar) value: LDS destinations stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 pieces of 128 x 128
-  int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int64_t arow = K * Fmt<FA>::bits / 8, brow = K * Fmt<FB>::bits / 8;
-  const int64_t nblk = K / 32;
-  const int nk = (int)(K / KS);
+  const int64_t M = g.M, N = g.N;
+  const uint32_t arow = (uint32_t)(g.K * Fmt<FA>::bits / 8), brow = (uint32_t)(g.K * Fmt<FB>::bits / 8);
+  const uint32_t nblk = (uint32_t)(g.K / 32);
+  const int nk = (int)(g.K / KS);                // stages per tile (>= NST)
+  const int nch = (nk + SPC - 1) / SPC;          // scale chunks per tile
+  const int T = g.tiles_m * g.tiles_n, G = gridDim.x, bid = blockIdx.x;
+  const int nt = (T - 1 - bid) / G + 1;          // tiles of this workgroup
 
   // this wave's panel segments I = wave + 4 k (A segments first, then B);
-  // lane chunk I * 64 + lane of the panel
-  const v4i ra = make_rsrc(aq, (uint32_t)(M * arow));
-  const v4i rb = make_rsrc(bq, (uint32_t)(N * brow));
+  // lane chunk I * 64 + lane of the panel, as an offset from the tile's first
+  // row
   uint32_t voff[SEGS];
   uint32_t lofs[SEGS];
   bool isb[SEGS];
@@ -825,41 +901,60 @@ __global__ __launch_bounds__(256) void k_gemm_fast(const uint8_t* __restrict__ a
     const int Lc = Ip * 64 + lane;
     const int r = Lc / ch, pc = Lc % ch;
     const int cc = pc ^ (isb[k] ? swz<C::CHB>(r) : swz<C::CHA>(r));
-    voff[k] = isb[k] ? (uint32_t)((n0 + r) * brow + 16 * cc) : (uint32_t)((m0 + r) * arow + 16 * cc);
+    voff[k] = (uint32_t)r * (isb[k] ? brow : arow) + 16 * cc;
     lofs[k] = (uint32_t)((isb[k] ? C::B_OFF : C::A_OFF) + Ip * 1024);
   }
   // scale chunks: wave w loads A scale rows 64 w .. 64 w + 63 and the same B
   // rows, 32 rows per load, lane pair (2 r, 2 r + 1) the two 16-byte halves of
   // row r's 32 bytes
-  const v4i rsa = make_rsrc(as, (uint32_t)(M * nblk));
-  const v4i rsb = make_rsrc(bs, (uint32_t)(N * nblk));
-  const uint32_t vsa = (uint32_t)((m0 + wave * 64 + (lane >> 1)) * nblk + 16 * (lane & 1));
-  const uint32_t vsb = (uint32_t)((n0 + wave * 64 + (lane >> 1)) * nblk + 16 * (lane & 1));
-  const uint32_t half_rows = (uint32_t)(32 * nblk);
+  const uint32_t vs0 = (uint32_t)(wave * 64 + (lane >> 1)) * nblk + 16 * (lane & 1);
+  const uint32_t vs1 = vs0 + 32 * nblk;
   const uint32_t lds0 = lds_addr(lds);
-  // Stage s into ring slot s % NST, preceded (first stage of a chunk) by the
-  // scale chunk s / SPC into scale buffer (s / SPC) % 2.  The scale loads are
-  // issued every stage under a mask that is empty except at chunk starts, so
-  // the loop body has no branch.  A stage past the end (s >= nk) goes through
-  // an empty buffer resource: every lane reads out of range, which fetches
-  // nothing, and the slot it fills is not read again.
   const v4i rnone = {0, 0, 0, 0x00020000};
-  // load j (0 .. NLD-1) of stage s: the four scale loads, then the panel
-  // segments
+
+  // Tile t of this workgroup: its first row of A and of B (M and N past the
+  // last tile, whose loads then fetch nothing).
+  struct TileAt { int m0, n0; };
+  auto tile_at = [&](int t) {
+    TileAt r{(int)M, (int)N};
+    if (t < nt) {
+      int tm, tn;
+      tile_of(bid + t * G, g.tiles_m, g.tiles_n, tm, tn);
+      r.m0 = tm * BM;
+      r.n0 = tn * BN;
+    }
+    return r;
+  };
+  // Buffer resources of a tile, each starting at the tile's first row and
+  // ending at the matrix's last: every row past M or N and every byte past
+  // the last scale row reads zero (past the last tile they are empty).
+  struct TileRs { v4i a, b, sa, sb; };
+  auto tile_rs = [&](TileAt o) {
+    TileRs r;
+    const uint32_t mr = (uint32_t)(M - o.m0), nr = (uint32_t)(N - o.n0);
+    r.a = make_rsrc(g.aq + (int64_t)o.m0 * arow, mr * arow);
+    r.b = make_rsrc(g.bq + (int64_t)o.n0 * brow, nr * brow);
+    r.sa = make_rsrc(g.as + (int64_t)o.m0 * nblk, mr * nblk);
+    r.sb = make_rsrc(g.bs + (int64_t)o.n0 * nblk, nr * nblk);
+    return r;
+  };
+  // Load j (0 .. NLD-1) of stage sl of the tile with resources r, into ring
+  // slot `slot`: the four scale loads (masked off except at the first stage
+  // of a chunk, so the loop body has no branch; chunk buffers alternate with
+  // the workgroup's running chunk count, parity `par`), then the panel
+  // segments.
   constexpr int NLD = 4 + SEGS;
-  auto issue_one = [&](int s, int j) {
-    const bool live = s < nk;
+  auto issue_one = [&](const TileRs& r, int sl, int par, int slot, int j) {
     if (j < 4) {
-      const bool chunk = live && (s % SPC) == 0;
-      const uint32_t sdst = lds0 + C::SC_OFF + ((s / SPC) & 1) * C::SC_BUF + wave * 64 * C::SC_ROW +
+      const bool chunk = (sl % SPC) == 0;
+      const uint32_t sdst = lds0 + C::SC_OFF + par * C::SC_BUF + wave * 64 * C::SC_ROW +
                             (j >> 1) * 256 * C::SC_ROW + (j & 1) * 32 * C::SC_ROW;
-      const uint32_t soff = chunk ? (uint32_t)(s / SPC) * C::SC_ROW + (j & 1) * half_rows : 0u;
-      dma16_if(j < 2 ? rsa : rsb, j < 2 ? vsa : vsb, soff, sdst, chunk);
+      const uint32_t vo = ((j & 1) ? vs1 : vs0) + (uint32_t)(sl / SPC) * C::SC_ROW;
+      dma16_if(j < 2 ? r.sa : r.sb, vo, 0u, sdst, chunk);
     } else {
       const int k = j - 4;
-      const uint32_t st = lds0 + (uint32_t)((s % NST) * C::STAGE);
-      const uint32_t kb0 = live ? (uint32_t)s * (isb[k] ? C::RBB : C::RBA) : 0u;
-      dma16(live ? (isb[k] ? rb : ra) : rnone, voff[k], kb0, st + lofs[k]);
+      dma16(isb[k] ? r.b : r.a, voff[k], (uint32_t)sl * (isb[k] ? C::RBB : C::RBA),
+            lds0 + (uint32_t)(slot * C::STAGE) + lofs[k]);
     }
   };
 
@@ -889,205 +984,230 @@ __global__ __launch_bounds__(256) void k_gemm_fast(const uint8_t* __restrict__ a
   constexpr int NB = SUB >= 4 ? 4 : 2;
   static_assert(SUB % NB == 0 && RA < NB, "operand register ring");
   Ops ops[NB];
-  ScaleWords<KS> sw;
-  auto slot = [&](int s) { return lds + (s % NST) * C::STAGE; };
+  ScaleWords<KS> sw, swn;
 
-  // prologue: stages 0 .. NST-1 in flight, wait for stage 0 (a wait counts
-  // panel loads only: masked-off scale loads may or may not count, and where
-  // they do the wait is merely longer), then substep (0, 0)'s operands
+  TileAt cur = tile_at(0), nxt = tile_at(1);
+  // prologue: stages 0 .. NST-1 of the first tile in flight, wait for stage 0
+  // (a wait counts panel loads only: masked-off scale loads may or may not
+  // count, and where they do the wait is merely longer), then the operands of
+  // its first RA substeps
 #pragma unroll
   for (int i = 0; i < NST; i++)
 #pragma unroll
-    for (int j = 0; j < NLD; j++) issue_one(i, j);
+    for (int j = 0; j < NLD; j++) issue_one(tile_rs(cur), i, (i / SPC) & 1, i, j);
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"((NST - 1) * SEGS) : "memory");
   __builtin_amdgcn_sched_barrier(0);
-  read_scale_words<C, FA, FB>(sw, lds, 0, w);
+  read_scale_words<C>(sw, lds, 0, 0, w);
   static_for<RA>([&](auto R) {
     constexpr int r = decltype(R)::value;
     scales_of<KS, FA == INT8>(ops[r], sw, r, w);
 #pragma unroll
-    for (int t = 0; t < 8; t++) read_tile<C, FA, FB>(ops[r], slot(0), r, t, w);
+    for (int t = 0; t < 8; t++) read_tile<C, FA, FB>(ops[r], lds, r, t, w);
   });
 
   // Per stage: SUB substeps.  Substep u's instructions run on ops[u % NB]
   // while the operands of the substep RA later are read into ops[(u + RA) %
   // NB], one tile after each of instructions 0-7.  Once the last operands of
-  // stage s are in (after instruction SK of substep SU), every wave waits for
-  // stage s + 1 (its own loads of it landed, its LDS reads back, then the
-  // barrier: every wave is also done reading slot s % NST) and reads stage
-  // s + 1's scale words; the loads of stage s + NST into that slot are then
-  // spread over the remaining instruction slots of the stage, while the last
-  // RA substeps read stage s + 1's first operands.  The loop body is one basic
-  // block; in the last stage the operands read for stage nk are never used.
+  // the stage are in (after instruction SK of substep SU), every wave waits
+  // for the next stage (its own loads of it landed, its LDS reads back, then
+  // the barrier: every wave is also done reading the current slot) and reads
+  // the next stage's scale words; the loads of the stage NST ahead (of this
+  // tile or the next) into the current slot are then spread over the
+  // remaining instruction slots of the stage, while the last RA substeps read
+  // the next stage's first operands.  In the last stage of the last tile the
+  // operands read for the stage after it are never used.
   constexpr int AHEAD = (NST - 2) * SEGS;  // panel loads still in flight at a wait
   constexpr int SU = SUB - 1 - RA;
   constexpr int SK = 11;
   constexpr int NSLOT = (15 - SK) + 16 * (SUB - 1 - SU);  // slots after the wait
-  ScaleWords<KS> swn;
-  for (int s = 0; s < nk; s++) {
+  int slot = 0;          // ring slot of the current stage
+  int64_t pm0 = M, pn0 = N;  // origin of the tile whose sums are in acc (none yet)
+  const int64_t wr = wm * 128, wc = wn * 128;
+
+  auto stage = [&](auto FIRST_, int t, int s) {
+    constexpr bool FIRST = decltype(FIRST_)::value;
+    // the next stage, whose scale words are read at the wait
+    const bool last = s + 1 == nk;
+    const int pn = ((last ? t + 1 : t) * nch + (last ? 0 : s + 1) / SPC) & 1;
+    const int on = ((last ? 0 : s + 1) % SPC) * (KS / 32);
+    // the stage NST ahead, loaded into this stage's slot after the wait
+    const bool cross = s + NST >= nk;
+    const int sl = cross ? s + NST - nk : s + NST;
+    const int lpar = ((cross ? t + 1 : t) * nch + sl / SPC) & 1;
+    const TileRs lr = tile_rs(cross ? nxt : cur);
+    const int cslot = slot, nslot = slot + 1 == NST ? 0 : slot + 1;
+    if constexpr (FIRST && MXO) {
+      // MX output: the previous tile's blocks go out before the first
+      // instruction of this one (the conversion needs whole tile rows)
+      if (t > 0) store_mx<OutMx<OUT>::fmt>(acc, MxOut{OutMx<OUT>::fmt, (uint8_t*)g.c, g.cs}, pm0 + wr,
+                                           pn0 + wc, M, N, lane);
+    }
     static_for<SUB>([&](auto U) {
       constexpr int u = decltype(U)::value;
       constexpr int un = (u + RA) % SUB;     // substep whose operands are read
-      constexpr bool next = u + RA >= SUB;   // ... of stage s + 1
-      Ops& nxt = ops[(u + RA) % NB];
-      const uint8_t* st = next ? slot(s + 1) : slot(s);
+      constexpr bool next = u + RA >= SUB;   // ... of the next stage
+      Ops& nx = ops[(u + RA) % NB];
+      const uint8_t* st = lds + (next ? nslot : cslot) * C::STAGE;
       auto body = [&](auto K) {
         constexpr int k = decltype(K)::value;
         if constexpr (u == SU && k == SK) {
           wait_all_barrier<AHEAD>();
-          read_scale_words<C, FA, FB>(swn, lds, s + 1, w);
+          read_scale_words<C>(swn, lds, pn, on, w);
         }
-        if constexpr (k < 8) read_tile<C, FA, FB>(nxt, st, un, k, w);
-        constexpr int g = (u - SU) * 16 + (k - SK - 1);  // slot index after the wait
-        if constexpr (g >= 0 && g < NSLOT) {
+        if constexpr (k < 8) read_tile<C, FA, FB>(nx, st, un, k, w);
+        constexpr int gi = (u - SU) * 16 + (k - SK - 1);  // slot index after the wait
+        if constexpr (gi >= 0 && gi < NSLOT) {
           static_for<NLD>([&](auto J) {
             constexpr int j = decltype(J)::value;
-            if constexpr ((j * NSLOT) / NLD == g) issue_one(s + NST, j);
+            if constexpr ((j * NSLOT) / NLD == gi) issue_one(lr, sl, lpar, cslot, j);
           });
         }
       };
+      // fp32 / bf16 output: the previous tile's results of acc[i][j] leave
+      // just before this tile's first instruction on acc[i][j] replaces them
+      auto pre = [&](auto K) {
+        constexpr int k = decltype(K)::value;
+        if constexpr (FIRST && u == 0 && !MXO)
+          store_tile<OUT, OUT == OUT_BF16>(acc[k >> 2][k & 3], g, pm0 + wr, pn0 + wc, k >> 2, k & 3, lane);
+      };
       if constexpr (FA == INT8)
-        substep_i8(acc, ops[u % NB], body);
+        substep_i8<FIRST && u == 0>(acc, ops[u % NB], pre, body);
       else
-        substep<FA, FB>(acc, ops[u % NB], body);
+        substep<FA, FB, FIRST && u == 0>(acc, ops[u % NB], pre, body);
       if constexpr (next)
-        scales_of<KS, FA == INT8>(nxt, swn, un, w);
+        scales_of<KS, FA == INT8>(nx, swn, un, w);
       else
-        scales_of<KS, FA == INT8>(nxt, sw, un, w);
+        scales_of<KS, FA == INT8>(nx, sw, un, w);
     });
     sw = swn;
+    slot = nslot;
+  };
+
+  for (int t = 0; t < nt; t++) {
+    if (t > 0) {
+      pm0 = cur.m0;
+      pn0 = cur.n0;
+      cur = nxt;
+      nxt = tile_at(t + 1);
+    }
+    stage(std::true_type{}, t, 0);
+    for (int s = 1; s < nk; s++) stage(std::false_type{}, t, s);
   }
   // the out-of-range loads of the last stages must be done before the
   // workgroup's LDS is released
   asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
 
-  // acc[i][j] is the 32 x 32 tile C^T[n][m]: lane l holds, for v = 4q + e,
-  // C[m0 + wm*128 + 32 i + l % 32][n0 + wn*128 + 32 j + 8 q + 4 (l / 32) + e]
-  if (mo.fmt == GEMM_OUT_BF16) {  // bf16 C, row pitch ldc elements
-    uint16_t* cb = (uint16_t*)mo.q;
-    const int lr = lane & 31;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int64_t row = m0 + wm * 128 + i * 32 + lr;
-      if (row >= M) continue;
-      uint16_t* crow = cb + row * ldc;
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-          const int64_t col = n0 + wn * 128 + j * 32 + 8 * q + 4 * w.kb;
-          const v16f& tt = acc[i][j];
-          if (vec_store && col + 3 < N) {
-            *(uint2*)(crow + col) = make_uint2(bf16x2_bits(tt[4 * q], tt[4 * q + 1]),
-                                               bf16x2_bits(tt[4 * q + 2], tt[4 * q + 3]));
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; e++)
-              if (col + e < N) crow[col + e] = bf16_bits(tt[4 * q + e]);
-          }
-        }
-      }
-    }
-    return;
-  }
-  if (mo.fmt >= 0) {  // wave-uniform: MX output
-    switch (mo.fmt) {
-      case E4M3: store_mx<E4M3>(acc, mo, m0 + wm * 128, n0 + wn * 128, M, N, lane); break;
-      case E5M2: store_mx<E5M2>(acc, mo, m0 + wm * 128, n0 + wn * 128, M, N, lane); break;
-      default: store_mx<E2M1>(acc, mo, m0 + wm * 128, n0 + wn * 128, M, N, lane); break;
-    }
-    return;
-  }
-  const int lr = lane & 31;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int64_t row = m0 + wm * 128 + i * 32 + lr;
-    if (row >= M) continue;
-    float* crow = c + row * ldc;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const int64_t col = n0 + wn * 128 + j * 32 + 8 * q + 4 * w.kb;
-        const v16f& tt = acc[i][j];
-        if (vec_store && col + 3 < N) {
-          *(float4*)(crow + col) = make_float4(tt[4 * q], tt[4 * q + 1], tt[4 * q + 2], tt[4 * q + 3]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; e++)
-            if (col + e < N) crow[col + e] = tt[4 * q + e];
-        }
-      }
-    }
+  // the last tile's results
+  if constexpr (MXO) {
+    store_mx<OutMx<OUT>::fmt>(acc, MxOut{OutMx<OUT>::fmt, (uint8_t*)g.c, g.cs}, cur.m0 + wr,
+                              cur.n0 + wc, M, N, lane);
+  } else {
+    static_for<16>([&](auto K) {
+      constexpr int k = decltype(K)::value;
+      store_tile<OUT>(acc[k >> 2][k & 3], g, cur.m0 + wr, cur.n0 + wc, k >> 2, k & 3, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   }
 }
 
-template <int FA, int FB, int KS>
-static hipError_t launch_fast(const void* aq, const uint8_t* as, const void* bq, const uint8_t* bs,
-                              int64_t M, int64_t N, int64_t K, float* c, int64_t ldc,
-                              int64_t tiles_m, int64_t tiles_n, const MxOut& mo, hipStream_t st) {
-  const int vec = mo.fmt == GEMM_OUT_BF16 ? ((uintptr_t)mo.q % 8) == 0 && ldc % 4 == 0
-                                            : ((uintptr_t)c % 16) == 0 && ldc % 4 == 0;
-  hipLaunchKernelGGL((k_gemm_fast<FA, FB, KS>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
-                     st, (const uint8_t*)aq, as, (const uint8_t*)bq, bs, M, N, K, c, ldc,
-                     (int)tiles_m, (int)tiles_n, vec, mo);
+// Compute units of the current device, looked up once per device.
+inline int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+template <int FA, int FB, int KS, int OUT>
+static hipError_t launch_fast(const GemmCall& gc, int64_t tiles_m, int64_t tiles_n) {
+  FastArgs g;
+  g.aq = (const uint8_t*)gc.aq;
+  g.as = gc.as;
+  g.bq = (const uint8_t*)gc.bq;
+  g.bs = gc.bs;
+  g.M = gc.M;
+  g.N = gc.N;
+  g.K = gc.K;
+  g.ldc = gc.ldc;
+  g.tiles_m = (int)tiles_m;
+  g.tiles_n = (int)tiles_n;
+  if (OUT == OUT_F32) {
+    g.c = gc.c;
+    g.cs = nullptr;
+    g.vec = ((uintptr_t)gc.c % 16) == 0 && gc.ldc % 4 == 0;
+  } else if (OUT == OUT_BF16) {
+    g.c = gc.out_q;
+    g.cs = nullptr;
+    g.vec = ((uintptr_t)gc.out_q % 8) == 0 && gc.ldc % 4 == 0;
+  } else {
+    g.c = gc.out_q;
+    g.cs = gc.out_s;
+    g.vec = 0;
+  }
+  // one workgroup per compute unit (a multiple of 8, so that a workgroup's
+  // tiles stay on its XCD), or one per tile when there are fewer tiles
+  const int64_t T = tiles_m * tiles_n;
+  int64_t G = device_cus() & ~7;
+  if (G < 8) G = 8;
+  if (T < G) G = T;
+  hipLaunchKernelGGL((k_gemm_fast<FA, FB, KS, OUT>), dim3((unsigned)G), dim3(256), 0, gc.st, g);
   return hipGetLastError();
 }
 
+template <int FA, int FB, int KS>
+static hipError_t launch_fast_out(const GemmCall& gc, int64_t tiles_m, int64_t tiles_n) {
+  switch (gc.out_fmt) {
+    case GEMM_OUT_BF16: return launch_fast<FA, FB, KS, OUT_BF16>(gc, tiles_m, tiles_n);
+    case E4M3: return launch_fast<FA, FB, KS, OUT_MX_E4M3>(gc, tiles_m, tiles_n);
+    case E5M2: return launch_fast<FA, FB, KS, OUT_MX_E5M2>(gc, tiles_m, tiles_n);
+    case E2M1: return launch_fast<FA, FB, KS, OUT_MX_E2M1>(gc, tiles_m, tiles_n);
+    default:
+      if (gc.out_fmt >= 0) return hipErrorNotSupported;
+      return launch_fast<FA, FB, KS, OUT_F32>(gc, tiles_m, tiles_n);
+  }
+}
+
 template <int FA, int FB>
-static hipError_t gemm_launch(const void* aq, const uint8_t* as, const void* bq, const uint8_t* bs,
-                              int64_t M, int64_t N, int64_t K, float* c, int64_t ldc,
-                              const MxOut& mo, hipStream_t st) {
+hipError_t gemm_launch(const GemmCall& gc) {
+  const int64_t M = gc.M, N = gc.N, K = gc.K;
   const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  // The fast path addresses operands and scales with 32-bit buffer offsets
-  // (rows rounded up to whole tiles, plus the reach of the last chunk, stay
-  // below 2^32 bytes) and loads scale rows 16 bytes at a time.
+  // The staged kernel addresses operands and scales with 32-bit buffer
+  // offsets (rows rounded up to whole tiles, plus the reach of the last chunk,
+  // stay below 2^32 bytes) and loads scale rows 16 bytes at a time.
   const int64_t lim = (int64_t)1 << 32;
   const int64_t nblk = K / 32;
-  const bool fast = K > 0 && K % 512 == 0 && ((uintptr_t)as % 16) == 0 &&
-                    ((uintptr_t)bs % 16) == 0 &&
+  const bool fast = K > 0 && K % 512 == 0 && ((uintptr_t)gc.as % 16) == 0 &&
+                    ((uintptr_t)gc.bs % 16) == 0 &&
                     tiles_m * BM * (K * Fmt<FA>::bits / 8) + K < lim &&
                     tiles_n * BN * (K * Fmt<FB>::bits / 8) + K < lim &&
                     tiles_m * BM * nblk + 64 < lim && tiles_n * BN * nblk + 64 < lim &&
                     tiles_m * tiles_n < ((int64_t)1 << 31);
   if (fast) {
     if constexpr (Fmt<FA>::bits == 4 && Fmt<FB>::bits == 4)
-      return launch_fast<FA, FB, 256>(aq, as, bq, bs, M, N, K, c, ldc, tiles_m, tiles_n, mo, st);
+      return launch_fast_out<FA, FB, 256>(gc, tiles_m, tiles_n);
     else
-      return launch_fast<FA, FB, 128>(aq, as, bq, bs, M, N, K, c, ldc, tiles_m, tiles_n, mo, st);
+      return launch_fast_out<FA, FB, 128>(gc, tiles_m, tiles_n);
   }
-  if (mo.fmt >= 0 && mo.fmt != GEMM_OUT_BF16) return hipErrorNotSupported;  // MX output: staged only
+  if (gc.out_fmt >= 0 && gc.out_fmt != GEMM_OUT_BF16) return hipErrorNotSupported;  // MX output: staged only
   if constexpr (FA == INT8) {
-    return gemm_i8_launch(aq, as, bq, bs, M, N, K, c, ldc, mo.fmt, mo.q, st);
+    return gemm_i8_launch<FA>(gc.aq, gc.as, gc.bq, gc.bs, M, N, K, gc.c, gc.ldc, gc.out_fmt, gc.out_q,
+                              gc.st);
   } else {
-    using L = GemmLds<FA, FB>;
-    static bool attr_done = false;  // benign race: the call is idempotent
-    if (!attr_done) {
-      hipError_t e = hipFuncSetAttribute((const void*)k_gemm<FA, FB>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
-      if (e != hipSuccess) return e;
-      attr_done = true;
-    }
-    hipLaunchKernelGGL((k_gemm<FA, FB>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), L::TOTAL,
-                       st, (const uint8_t*)aq, as, (const uint8_t*)bq, bs, M, N, K, c,
-                       mo.fmt == GEMM_OUT_BF16 ? (uint16_t*)mo.q : nullptr, ldc, (int)tiles_n);
+    hipLaunchKernelGGL((k_gemm<FA, FB>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, gc.st,
+                       (const uint8_t*)gc.aq, gc.as, (const uint8_t*)gc.bq, gc.bs, M, N, K, gc.c,
+                       gc.out_fmt == GEMM_OUT_BF16 ? (uint16_t*)gc.out_q : nullptr, gc.ldc,
+                       (int)tiles_n);
     return hipGetLastError();
   }
-}
-
-hipError_t launch_gemm(const void* aq, const uint8_t* as, int fa, const void* bq,
-                       const uint8_t* bs, int fb, int64_t M, int64_t N, int64_t K, float* c,
-                       int64_t ldc, int out_fmt, uint8_t* out_q, uint8_t* out_s, hipStream_t st) {
-  const MxOut mo{out_fmt, out_q, out_s};
-  if (fa == INT8 && fb == INT8) return gemm_launch<INT8, INT8>(aq, as, bq, bs, M, N, K, c, ldc, mo, st);
-#define MX_G(A, B) \
-  if (fa == A && fb == B) return gemm_launch<A, B>(aq, as, bq, bs, M, N, K, c, ldc, mo, st);
-#define MX_GA(A) MX_G(A, E4M3) MX_G(A, E5M2) MX_G(A, E2M3) MX_G(A, E3M2) MX_G(A, E2M1)
-  MX_GA(E4M3) MX_GA(E5M2) MX_GA(E2M3) MX_GA(E3M2) MX_GA(E2M1)
-#undef MX_GA
-#undef MX_G
-  return hipErrorInvalidValue;
 }
 
 }  // namespace mx

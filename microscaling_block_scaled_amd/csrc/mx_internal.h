@@ -35,6 +35,25 @@ hipError_t launch_gemm(const void* a_q, const uint8_t* a_s, int a_fmt, const voi
                        const uint8_t* b_s, int b_fmt, int64_t M, int64_t N, int64_t K, float* c,
                        int64_t ldc, int out_fmt, uint8_t* out_q, uint8_t* out_s, hipStream_t st);
 
+// One GEMM call as the kernels' launchers take it (K already a multiple of 32).
+struct GemmCall {
+  const void* aq;
+  const uint8_t* as;
+  const void* bq;
+  const uint8_t* bs;
+  int64_t M, N, K;
+  float* c;
+  int64_t ldc;
+  int out_fmt;
+  uint8_t* out_q;
+  uint8_t* out_s;
+  hipStream_t st;
+};
+// Launcher of one operand-format pair (explicitly instantiated per pair by
+// the build, from mx_gemm_kernels.hpp).
+template <int FA, int FB>
+hipError_t gemm_launch(const GemmCall& gc);
+
 inline int elem_bits(int fmt) { return fmt == 2 || fmt == 3 ? 6 : (fmt == 4 ? 4 : 8); }
 
 }  // namespace mx

@@ -178,7 +178,12 @@ __device__ __forceinline__ void hadamard_local(uint32_t v[32], uint32_t signs) {
 // ---------------------------------------------------------------------------
 struct QP {
   const uint8_t* x;
+  // rows, cols: the source's extent padded to whole blocks (multiples of 32);
+  // they give every pitch, block count and stochastic-rounding index.
+  // rows_x, cols_x: the extent that exists in memory; elements past it read
+  // as +0 (a short last block is padded with zeros).
   int64_t rows, cols, ld_bytes;
+  int64_t rows_x, cols_x;
   uint8_t* q_row;
   int64_t qr_pitch;  // bytes per packed output row (row-wise layout)
   uint8_t* s_row;
@@ -295,6 +300,33 @@ __device__ __forceinline__ void store32_stream(uint8_t* p, const Pack8 o[4]) {
   }
 }
 
+// `n` elements (8 or 32) of ESZ bytes at src into raw words (two bf16 or one
+// fp32 per word), of which the first `valid` exist and the rest read +0: whole
+// 16-byte loads when all exist, else element by element (only the short last
+// block of a row or tile).
+template <int ESZ, int n, bool NT>
+__device__ __forceinline__ void load_elems(const uint8_t* src, int valid, uint32_t* raw) {
+  constexpr int W = n * ESZ / 4;  // words
+  if (valid >= n) {
+#pragma unroll
+    for (int j = 0; j < W / 4; j++) {
+      const uint4 t = NT ? ld_stream(src + 16 * j) : *(const uint4*)(src + 16 * j);
+      raw[4 * j] = t.x; raw[4 * j + 1] = t.y; raw[4 * j + 2] = t.z; raw[4 * j + 3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < W; w++) {
+      if (ESZ == 4) {
+        raw[w] = w < valid ? *(const uint32_t*)(src + 4 * w) : 0u;
+      } else {
+        const uint32_t lo = 2 * w < valid ? *(const uint16_t*)(src + 4 * w) : 0u;
+        const uint32_t hi = 2 * w + 1 < valid ? *(const uint16_t*)(src + 4 * w + 2) : 0u;
+        raw[w] = lo | (hi << 16);
+      }
+    }
+  }
+}
+
 template <int SRC, int F, bool SR, bool HAD>
 __global__ __launch_bounds__(256) void k_quant_blocks(QP p) {
   constexpr int ESZ = SRC == SRC_BF16 ? 2 : 4;
@@ -308,14 +340,10 @@ __global__ __launch_bounds__(256) void k_quant_blocks(QP p) {
   const int64_t r = g / wpr;
   const int64_t kb = (int64_t)(g % wpr) * 64 + lane;  // block of row r
   const int64_t bpr = p.cols >> 5;
-  if (r >= p.rows || kb >= bpr) return;  // no lane exchanges below
+  if (r >= p.rows_x || kb >= bpr) return;  // no lane exchanges below
   const uint8_t* src = p.x + r * p.ld_bytes + kb * 32 * ESZ;
   uint32_t raw[8 * ESZ];
-#pragma unroll
-  for (int j = 0; j < 2 * ESZ; j++) {
-    const uint4 t = *(const uint4*)(src + 16 * j);
-    raw[4 * j] = t.x; raw[4 * j + 1] = t.y; raw[4 * j + 2] = t.z; raw[4 * j + 3] = t.w;
-  }
+  load_elems<ESZ, 32, false>(src, (int)(p.cols_x - kb * 32 < 32 ? p.cols_x - kb * 32 : 32), raw);
   uint32_t v[32];
   uint32_t am = 0;
   if constexpr (PACKED) {
@@ -565,6 +593,7 @@ __device__ __forceinline__ void col_pair_sr(const QP& p, const uint32_t w[32], i
   } else {
 #pragma unroll
     for (int k = 0; k < 2; k++) {
+      if (col + k >= p.cols_x) break;  // a column past the source's end
       p.s_colt[(col + k) * (p.rows >> 5) + (rs >> 5)] = (uint8_t)code[k];
       store32<F>(p.q_colt + (col + k) * p.qc_pitch + (rs * Fmt<F>::bits) / 8, o[k]);
     }
@@ -644,8 +673,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SR && SRC =
   const int tid = threadIdx.x;
   const int64_t tr = blockIdx.x / p.tiles_c, tc = blockIdx.x % p.tiles_c;
   const int64_t r0 = tr * T::TR, c0 = tc * T::TC;
-  const int tr_eff = (int)(p.rows - r0 < T::TR ? p.rows - r0 : T::TR);
-  const int tc_eff = (int)(p.cols - c0 < T::TC ? p.cols - c0 : T::TC);
+  // rows / columns of the tile that exist, and the same padded to whole
+  // blocks (the padding reads +0)
+  const int tr_eff = (int)(p.rows_x - r0 < T::TR ? p.rows_x - r0 : T::TR);
+  const int tc_eff = (int)(p.cols_x - c0 < T::TC ? p.cols_x - c0 : T::TC);
+  const int tr_pad = (int)(p.rows - r0 < T::TR ? p.rows - r0 : T::TR);
+  const int tc_pad = (int)(p.cols - c0 < T::TC ? p.cols - c0 : T::TC);
   const bool whole = tr_eff == T::TR && tc_eff == T::TC;
   // whole bf16 tiles with rows of s_row in whole dwords: the row-wise scales
   // are gathered in LDS and written one dword per row
@@ -654,22 +687,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SR && SRC =
   const bool gather = FAST && ROWS && whole && (p.cols & 127) == 0;
   const int cq = tid % T::CPRW, sub = tid / T::CPRW;
   const HadLane hl = had_lane(p.signs, cq & 3);  // tile columns start at a multiple of 4 chunks
-  const bool col_ok = cq * 8 < tc_eff;
+  // chunk cq (8 elements) takes part when it lies in a block of the padded
+  // tile; `valid` of its elements exist
+  const bool col_ok = cq * 8 < tc_pad;
+  const int valid = tc_eff - cq * 8;
 
   uint32_t raw[T::PASSES][T::RAWN];
 #pragma unroll
   for (int pp = 0; pp < T::PASSES; pp++) {
     const int row = pp * T::RPP + sub;
-    if (row < tr_eff && col_ok) {
-      const uint8_t* src = p.x + (r0 + row) * p.ld_bytes + c0 * T::ESZ;
-      if constexpr (SRC == SRC_BF16) {
-        const uint4 t = ld_stream(src + 16 * cq);
-        raw[pp][0] = t.x; raw[pp][1] = t.y; raw[pp][2] = t.z; raw[pp][3] = t.w;
+    if (row < tr_pad && col_ok) {
+      if (row < tr_eff && valid > 0) {
+        const uint8_t* src = p.x + (r0 + row) * p.ld_bytes + (c0 + 8 * cq) * T::ESZ;
+        load_elems<T::ESZ, 8, true>(src, valid, raw[pp]);
       } else {
-        const uint4 t0 = ld_stream(src + 32 * cq);
-        const uint4 t1 = ld_stream(src + 32 * cq + 16);
-        raw[pp][0] = t0.x; raw[pp][1] = t0.y; raw[pp][2] = t0.z; raw[pp][3] = t0.w;
-        raw[pp][4] = t1.x; raw[pp][5] = t1.y; raw[pp][6] = t1.z; raw[pp][7] = t1.w;
+#pragma unroll
+        for (int k = 0; k < T::RAWN; k++) raw[pp][k] = 0u;
       }
     }
   }
@@ -680,10 +713,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SR && SRC =
 #pragma unroll
   for (int pp = 0; pp < T::PASSES; pp++) {
     const int row = pp * T::RPP + sub;
-    if (row < tr_eff && col_ok) {
+    if (row < tr_pad && col_ok) {
       uint32_t v[8];
       widen8<SRC>(raw[pp], v);
-      if (ROWS) {
+      if (ROWS && row < tr_eff) {
         if constexpr (FAST) {
           row_chunk_bf16<F>(p, r0 + row, (c0 >> 3) + cq, raw[pp],
                             gather ? (uint8_t*)sc_lds + 4 * row + (cq >> 2) : nullptr);
@@ -744,7 +777,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SR && SRC =
 #pragma unroll
           for (int i = 0; i < 32; i++)
             v[i] = SRC == SRC_BF16 ? (k == 0 ? w[i] << 16 : w[i] & 0xFFFF0000u) : w[i];
-          col_block<F, SR, HAD>(p, v, c0 + g * T::CPT + k, r0 + 32 * qb);
+          if (c0 + g * T::CPT + k < p.cols_x) col_block<F, SR, HAD>(p, v, c0 + g * T::CPT + k, r0 + 32 * qb);
         }
       }
     }
@@ -757,15 +790,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SR && SRC =
 static QP make_qp(const QuantArgs& a) {
   QP p{};
   p.x = (const uint8_t*)a.x;
-  p.rows = a.rows;
-  p.cols = a.cols;
+  p.rows_x = a.rows;
+  p.cols_x = a.cols;
+  p.rows = (a.rows + 31) / 32 * 32;
+  p.cols = (a.cols + 31) / 32 * 32;
   p.ld_bytes = a.ld_bytes;
   const int bits = elem_bits(a.fmt);
   p.q_row = a.q_row;
-  p.qr_pitch = a.cols * bits / 8;
+  p.qr_pitch = p.cols * bits / 8;
   p.s_row = a.s_row;
   p.q_colt = a.q_colt;
-  p.qc_pitch = a.rows * bits / 8;
+  p.qc_pitch = p.rows * bits / 8;
   p.s_colt = a.s_colt;
   p.seed = a.seed;
   p.off = a.counter_offset;
@@ -778,7 +813,7 @@ static hipError_t rows_launch(const QP& p0, hipStream_t st) {
   QP p = p0;
   const int64_t wpr = (p.cols / 32 + 63) / 64;  // waves per row, 64 blocks each
   p.wpr = (int)wpr;
-  const int64_t waves = p.rows * wpr;
+  const int64_t waves = p.rows_x * wpr;
   if (waves >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_quant_blocks<SRC, F, SR, HAD>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, p);
   return hipGetLastError();

@@ -105,8 +105,9 @@ def quantize(x: torch.Tensor, fmt: int, layouts: int = LAYOUT_ROW, round_mode: i
              hadamard: bool = False, hadamard_signs: int = 0, seed: int = 0,
              counter_offset: int = 0, out: dict | None = None, stream=None) -> dict:
     """MX-quantize a 2-D fp32/bf16 device tensor.  Returns uint8 device tensors
-    q_row [rows, packed cols], s_row [rows, cols/32] and/or q_colt [cols, packed
-    rows], s_colt [cols, rows/32]; ``out`` may supply them preallocated."""
+    q_row [rows, packed cols], s_row [rows, blocks of cols] and/or q_colt [cols,
+    packed rows], s_colt [cols, blocks of rows]; a short last block is padded
+    with zeros to 32 elements.  ``out`` may supply them preallocated."""
     if x.dim() != 2 or x.dtype not in (torch.float32, torch.bfloat16) or not x.is_cuda:
         raise ValueError("x must be a 2-D fp32/bf16 CUDA tensor")
     if x.stride(1) != 1:
@@ -116,11 +117,11 @@ def quantize(x: torch.Tensor, fmt: int, layouts: int = LAYOUT_ROW, round_mode: i
     o = dict(out or {})
     dev = x.device
     if layouts & LAYOUT_ROW and "q_row" not in o:
-        o["q_row"] = torch.empty((rows, cols * BITS[fmt] // 8), dtype=torch.uint8, device=dev)
-        o["s_row"] = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+        o["q_row"] = torch.empty((rows, packed_bytes(fmt, 1, cols)), dtype=torch.uint8, device=dev)
+        o["s_row"] = torch.empty((rows, scale_bytes(1, cols)), dtype=torch.uint8, device=dev)
     if layouts & LAYOUT_COLT and "q_colt" not in o:
-        o["q_colt"] = torch.empty((cols, rows * BITS[fmt] // 8), dtype=torch.uint8, device=dev)
-        o["s_colt"] = torch.empty((cols, rows // 32), dtype=torch.uint8, device=dev)
+        o["q_colt"] = torch.empty((cols, packed_bytes(fmt, 1, rows)), dtype=torch.uint8, device=dev)
+        o["s_colt"] = torch.empty((cols, scale_bytes(1, rows)), dtype=torch.uint8, device=dev)
     p = QuantParams(src, fmt, layouts, round_mode, FLAG_HADAMARD32 if hadamard else 0,
                     hadamard_signs & 0xFFFFFFFF, seed, counter_offset)
     st = lib.mx_quantize(_ptr(x), rows, cols, x.stride(0), ctypes.byref(p),
@@ -171,13 +172,13 @@ def gemm_mx(a_q: torch.Tensor, a_s: torch.Tensor, a_fmt: int, b_q: torch.Tensor,
             out: dict | None = None, stream=None) -> dict:
     """The product of ``gemm`` quantized row-wise (blocks of 32 along N, round to
     nearest even) into format ``c_fmt`` inside the GEMM.  Returns uint8 device
-    tensors q_row [M, N * bits / 8] and s_row [M, N / 32]; ``out`` may supply
-    them preallocated."""
+    tensors q_row [M, packed N] and s_row [M, blocks of N] (a short last block
+    padded); ``out`` may supply them preallocated."""
     o = dict(out or {})
     dev = a_q.device
     if "q_row" not in o:
-        o["q_row"] = torch.empty((M, N * BITS[c_fmt] // 8), dtype=torch.uint8, device=dev)
-        o["s_row"] = torch.empty((M, N // 32), dtype=torch.uint8, device=dev)
+        o["q_row"] = torch.empty((M, packed_bytes(c_fmt, 1, N)), dtype=torch.uint8, device=dev)
+        o["s_row"] = torch.empty((M, scale_bytes(1, N)), dtype=torch.uint8, device=dev)
     _check(lib.mx_gemm_mx(_ptr(a_q), _ptr(a_s), a_fmt, _ptr(b_q), _ptr(b_s), b_fmt, M, N, K,
                           c_fmt, _ptr(o["q_row"]), _ptr(o["s_row"]), _stream(stream)),
            "mx_gemm_mx")

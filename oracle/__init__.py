@@ -75,8 +75,16 @@ def _load():
     lib.mxo_gemm_f64.argtypes = [P, P, ctypes.c_int, P, P, ctypes.c_int, i64, i64, i64, P, P]
     lib.mxo_gemm_f64_at.argtypes = [P, P, ctypes.c_int, P, P, ctypes.c_int, i64, i64, i64,
                                     P, P, i64, P, P]
+    lib.mxo_set_threads.restype = ctypes.c_int
+    lib.mxo_set_threads.argtypes = [ctypes.c_int]
     _lib = lib
     return lib
+
+
+def set_threads(n: int = 0) -> int:
+    """OpenMP threads of the whole-tensor functions (0: unchanged); returns
+    the count in force."""
+    return int(_load().mxo_set_threads(n))
 
 
 def _ptr(a: np.ndarray):

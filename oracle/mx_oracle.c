@@ -32,6 +32,7 @@
 #include "mx_oracle.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -412,4 +413,11 @@ int mxo_gemm_f64_at(const uint8_t* a_q, const uint8_t* a_s, int a_fmt, const uin
   for (int64_t i = 0; i < count; i++)
     dot_f64(a_q, a_s, a_fmt, b_q, b_s, b_fmt, K, ms[i], ns[i], &c[i], t ? &t[i] : NULL);
   return 0;
+}
+
+/* OpenMP threads the whole-tensor functions use (for timing the oracle on one
+ * core and on all of them); returns the count now in force. */
+int mxo_set_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
+  return omp_get_max_threads();
 }

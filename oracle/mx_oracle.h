@@ -121,6 +121,10 @@ int mxo_gemm_f64_at(const uint8_t* a_q, const uint8_t* a_s, int a_fmt,
                     const int64_t* ms, const int64_t* ns, int64_t count,
                     double* c, double* t);
 
+/* Threads of the whole-tensor functions (n <= 0 leaves them unchanged);
+ * returns the number in force. */
+int mxo_set_threads(int n);
+
 #ifdef __cplusplus
 }
 #endif

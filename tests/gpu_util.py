@@ -1,5 +1,5 @@
-"""Helpers shared by the GPU parity tests: host <-> device marshalling and the
-GEMM tolerance.  No MX arithmetic here."""
+"""Helpers shared by the GPU parity tests: host <-> device marshalling, guard
+bands around outputs, and the GEMM tolerance.  No MX arithmetic here."""
 import numpy as np
 import torch
 
@@ -31,6 +31,58 @@ def assert_same_bits(got: dict, want: dict, what: str = ""):
                                  f"gpu {g[i]:#x} oracle {w[i]:#x}")
 
 
+# ---------------------------------------------------------------------------
+# guard bands: an output tensor placed inside a larger buffer whose margins
+# hold a known byte, checked after the call (writes past either end show up)
+# ---------------------------------------------------------------------------
+GUARD = 4096  # bytes on each side; a multiple of 16 keeps the view 16-byte aligned
+CANARY = 0xA5
+
+
+class Guarded:
+    """A [shape] tensor of `dtype` inside a byte buffer with GUARD canary bytes
+    before and after it.  ``t`` is the view handed to the library."""
+
+    def __init__(self, shape, dtype=torch.uint8):
+        esz = torch.empty((), dtype=dtype).element_size()
+        n = int(np.prod(shape)) if len(shape) else 1
+        nbytes = n * esz
+        self.lo, self.hi = GUARD, GUARD + ((nbytes + 15) // 16) * 16
+        self.buf = torch.full((self.hi + GUARD,), CANARY, dtype=torch.uint8, device="cuda")
+        self.t = self.buf[self.lo:self.lo + nbytes].view(dtype).view(shape)
+        self.nbytes = nbytes
+
+    def check(self, what=""):
+        b = host(self.buf)
+        before = b[:self.lo]
+        after = b[self.lo + self.nbytes:]
+        if not (before == CANARY).all():
+            raise AssertionError(f"{what}: {(before != CANARY).sum()} bytes written before the output")
+        if not (after == CANARY).all():
+            raise AssertionError(f"{what}: {(after != CANARY).sum()} bytes written past the output")
+
+
+def guarded_quant_out(mx, fmt, rows, cols, layouts):
+    """Guarded output tensors for mx.quantize (padded pitch for partial blocks)."""
+    o = {}
+    nbr, nbc = (cols + 31) // 32, (rows + 31) // 32
+    if layouts & 1:
+        o["q_row"] = Guarded((rows, nbr * 32 * mx.BITS[fmt] // 8))
+        o["s_row"] = Guarded((rows, nbr))
+    if layouts & 2:
+        o["q_colt"] = Guarded((cols, nbc * 32 * mx.BITS[fmt] // 8))
+        o["s_colt"] = Guarded((cols, nbc))
+    return o
+
+
+def check_guards(g: dict, what=""):
+    for k, v in g.items():
+        v.check(f"{what} {k}")
+
+
+# ---------------------------------------------------------------------------
+# GEMM tolerance
+# ---------------------------------------------------------------------------
 def gemm_tolerance(t):
     """|err| <= 1e-5 * sum|a*b| per element, plus 2^-126 for fp32 underflow."""
     return 1e-5 * t + 2.0 ** -126
@@ -41,13 +93,14 @@ def mfma_group_bound(a, b, pairs=None):
     for C = a @ b.T (a [M,K], b [N,K] dequantized, fp64), per element of C (or
     per (m, n) in `pairs`).
 
-    Measured on gfx950 (see the design notes): the instruction adds each
-    aligned group of 8 consecutive K products after truncating every product
-    toward zero to a multiple of q = 2^(E - 13), E the exponent of the group's
-    largest product; groups then add exactly.  Where a product is not a
-    multiple of q it may lose up to q; products that are multiples of q (for
-    E2M1 and E2M3 operands, all of them) lose nothing, so those pairs keep
-    the plain tolerance."""
+    Measured on gfx950: the instruction adds each aligned group of 8
+    consecutive K products after truncating every product toward zero to a
+    multiple of q = 2^(E - 13), E the exponent of the group's largest product;
+    groups then add exactly.  Where a product is not a multiple of q it may
+    lose up to q; products that are multiples of q (for E2M1 and E2M3
+    operands, all of them) lose nothing.  Used only by the tests that cover
+    the short-K shapes where this truncation alone can exceed the
+    1e-5 * sum|a*b| contract."""
     if pairs is None:
         ms, ns = np.repeat(np.arange(a.shape[0]), b.shape[0]), np.tile(np.arange(b.shape[0]), a.shape[0])
         shape = (a.shape[0], b.shape[0])
@@ -69,14 +122,28 @@ def mfma_group_bound(a, b, pairs=None):
     return out.reshape(shape)
 
 
+def gemm_report(c_gpu, c_ref, t_ref):
+    """(worst |err| / (1e-5 sum|ab| + 2^-126), elements over the plain bound,
+    worst |err| / sum|ab|)."""
+    c_gpu = np.asarray(c_gpu, dtype=np.float64)
+    err = np.abs(c_gpu - c_ref)
+    r = err / gemm_tolerance(t_ref)
+    r = np.where(np.isnan(r), np.inf, r)
+    rel = err / np.maximum(t_ref, 1e-300)
+    return float(np.max(r)) if r.size else 0.0, int((r > 1.0).sum()), float(np.max(rel)) if rel.size else 0.0
+
+
 def assert_gemm_close(c_gpu, c_ref, t_ref, what="", extra=None):
+    """Every element within 1e-5 * sum|a*b| + 2^-126 (plus `extra`, only where
+    a test covers the instruction's short-K truncation); returns the worst
+    |err| / sum|a*b|."""
     c_gpu = np.asarray(c_gpu, dtype=np.float64)
     err = np.abs(c_gpu - c_ref)
     tol = gemm_tolerance(t_ref) if extra is None else gemm_tolerance(t_ref) + extra
     bad = ~(err <= tol)
     if bad.any():
         i = np.argwhere(bad)[0]
-        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside 1e-5*sum|ab|; first at "
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside the bound; first at "
                              f"{tuple(i)}: gpu {c_gpu[tuple(i)]} ref {c_ref[tuple(i)]} "
                              f"sum|ab| {t_ref[tuple(i)]}")
-    return float(np.max(err / np.maximum(t_ref, 1e-300)))
+    return float(np.max(err / np.maximum(t_ref, 1e-300))) if err.size else 0.0

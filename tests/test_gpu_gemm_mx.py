@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import dev, gemm_tolerance, host, mfma_group_bound, say
+from gpu_util import dev, gemm_tolerance, host, say
 from test_gpu_gemm import FMT_NAMES, quant_pair
 
 pytestmark = pytest.mark.gpu
@@ -105,10 +105,8 @@ def test_mx_output_small(mx, oracle, fa, fw, fc):
         torch.cuda.synchronize()
         cref, t = oracle.gemm_f64(oa["q_row"], oa["s_row"], fa, ow["q_row"], ow["s_row"], fw,
                                   M, N, K)
-        extra = mfma_group_bound(oracle.dequantize(oa["q_row"], oa["s_row"], fa, M, K).astype(np.float64),
-                                 oracle.dequantize(ow["q_row"], ow["s_row"], fw, N, K).astype(np.float64))
         check_against_oracle(oracle, fc, host(got["q_row"]), host(got["s_row"]), cref,
-                             gemm_tolerance(t) + extra, what)
+                             gemm_tolerance(t), what)
         assert (host(got["s_row"])[M // 2] == 0).all() and (host(got["q_row"])[M // 2] == 0).all()
         say("gemm + quantize", what)
         same_as_two_kernels(mx, ga, fa, gw, fw, M, N, K, fc, got, what)
@@ -168,12 +166,7 @@ def test_mx_output_full_size(mx, oracle, cfg, fc):
     ns = (blks[:, None] * 32 + np.arange(32)[None, :]).reshape(-1)
     cref, t = oracle.gemm_f64_at(oa["q_row"], oa["s_row"], fa, ow["q_row"], ow["s_row"], fw,
                                  M, N, K, ms, ns)
-    S = len(ms)
-    ad = oracle.dequantize(np.ascontiguousarray(oa["q_row"][ms]), np.ascontiguousarray(oa["s_row"][ms]),
-                           fa, S, K).astype(np.float64)
-    wd = oracle.dequantize(np.ascontiguousarray(ow["q_row"][ns]), np.ascontiguousarray(ow["s_row"][ns]),
-                           fw, S, K).astype(np.float64)
-    tol = gemm_tolerance(t) + mfma_group_bound(ad, wd, pairs=(np.arange(S), np.arange(S)))
+    tol = gemm_tolerance(t)
     # the sampled blocks' codes and scales, as one [samples x 32] output
     qh, sh = host(got["q_row"]), host(got["s_row"])
     bpb = 32 * oracle.elem_bits(fc) // 8  # bytes per block

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import assert_same_bits, dev, host, say
+from gpu_util import assert_same_bits, check_guards, dev, guarded_quant_out, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -214,3 +214,98 @@ def test_full_size_fp4_recipe(mx, oracle):
     d = make("mxfp4_mlp")
     run_both(mx, oracle, d["W"], 4, 1, 0, True, 0, 0, 0, what="W 4096x14336 h32 rne")
     run_both(mx, oracle, d["A"], 4, 1, 1, True, 0, 42, 0, what="A 8192x14336 h32 sr")
+
+
+@pytest.mark.parametrize("fmt", range(6))
+def test_strided_source_and_guards(mx, oracle, fmt):
+    """The source is a column slice of a wider tensor (ld_x > cols, the slice
+    starting 32 bytes in), in bf16 and fp32, every layout, RNE and SR with the
+    transform; every output sits inside canary guard bands, so a write past
+    either end of q_row / s_row / q_colt / s_colt fails."""
+    from microscaling_block_scaled_amd.synth import make
+    wide = make("quant_sweep", {"X": (288, 480)}, seed=11)["X"]
+    rng = np.random.default_rng(40 + fmt)
+    wide32 = (rng.standard_t(3, (160, 352)) * np.exp2(rng.uniform(-30, 30, (160, 1)))).astype(np.float32)
+    for src, c0, cols in ((wide, 16, 416), (wide32, 8, 288)):
+        rows = src.shape[0]
+        xd = dev(src)[:, c0:c0 + cols]
+        assert xd.stride(0) == src.shape[1]
+        x = np.ascontiguousarray(src[:, c0:c0 + cols])
+        for lay in (1, 2, 3):
+            for rnd, had in ((0, False), (1, True)):
+                say("quantize strided", src.dtype, x.shape, "ld", src.shape[1], FMT_NAMES[fmt], lay, rnd, had)
+                g = guarded_quant_out(mx, fmt, rows, cols, lay)
+                got = mx.quantize(xd, fmt, lay, rnd, had, 0x13579BDF, 5, 2,
+                                  out={k: v.t for k, v in g.items()})
+                torch.cuda.synchronize()
+                check_guards(g, "strided")
+                want = oracle.quantize(x, fmt, lay, rnd, oracle.FLAG_HADAMARD32 if had else 0, 5, 2,
+                                       0x13579BDF)
+                assert_same_bits(got, want, f"strided lay{lay}")
+
+
+# ---------------------------------------------------------------------------
+# partial blocks: a blocked dimension that is not a multiple of 32
+# ---------------------------------------------------------------------------
+PARTIAL_SHAPES = [(40, 70), (33, 65), (7, 31), (130, 300), (288, 417), (5, 1), (160, 129)]
+
+
+def slack_source(x, esz):
+    """x inside a wider array whose row pitch is a multiple of 16 bytes, the
+    columns past x's end holding NaN / Inf / huge values: the kernels must
+    never read them (they would change the block maxima)."""
+    rows, cols = x.shape
+    step = 16 // esz
+    ld = (cols + step - 1) // step * step + step
+    if x.dtype == np.uint16:
+        wide = np.full((rows, ld), 0x7FC0, np.uint16)
+        wide[:, cols + 1:] = 0x7F80
+    else:
+        wide = np.full((rows, ld), np.nan, np.float32)
+        wide[:, cols + 1:] = np.float32(3e38)
+    wide[:, :cols] = x
+    return wide
+
+
+@pytest.mark.parametrize("fmt", range(6))
+def test_partial_blocks(mx, oracle, fmt):
+    """Ragged rows and columns (short last blocks, read as zero padding), bf16
+    and fp32, every layout, RNE / SR / SR with the transform, sources with
+    poisoned slack past the last column, outputs inside guard bands."""
+    from microscaling_block_scaled_amd.synth import make
+    rng = np.random.default_rng(300 + fmt)
+    for bf16 in (True, False):
+        for rows, cols in PARTIAL_SHAPES:
+            if bf16:
+                x = make("quant_sweep", {"X": (rows, cols)}, seed=rows + cols)["X"]
+            else:
+                x = (rng.standard_t(3, (rows, cols)) * np.exp2(rng.uniform(-30, 30, (rows, 1)))).astype(np.float32)
+            wide = slack_source(x, 2 if bf16 else 4)
+            xd = dev(wide)[:, :cols]
+            for lay in (1, 2, 3):
+                for rnd, had in ((0, False), (1, False), (1, True)):
+                    say("partial", "bf16" if bf16 else "f32", rows, cols, FMT_NAMES[fmt], lay, rnd, had)
+                    g = guarded_quant_out(mx, fmt, rows, cols, lay)
+                    got = mx.quantize(xd, fmt, lay, rnd, had, 0x2468ACE1, 77, 5,
+                                      out={k: v.t for k, v in g.items()})
+                    torch.cuda.synchronize()
+                    check_guards(g, f"partial {rows}x{cols}")
+                    want = oracle.quantize(x, fmt, lay, rnd, oracle.FLAG_HADAMARD32 if had else 0, 77, 5,
+                                           0x2468ACE1)
+                    assert_same_bits(got, want, f"partial {rows}x{cols} lay{lay} rnd{rnd} h{had}")
+
+
+@pytest.mark.parametrize("fmt", range(6))
+def test_dequantize_partial_blocks(mx, oracle, fmt):
+    rng = np.random.default_rng(400 + fmt)
+    for rows, cols in [(9, 70), (33, 1), (64, 100), (3, 97)]:
+        cp = (cols + 31) // 32 * 32
+        from microscaling_block_scaled_amd import mx as m
+        q = rng.integers(0, 256, (rows, cp * m.BITS[fmt] // 8), dtype=np.uint8)
+        s = rng.integers(100, 150, (rows, cp // 32), dtype=np.uint8)
+        say("dequantize partial", FMT_NAMES[fmt], rows, cols)
+        y = host(mx.dequantize(dev(q), dev(s), fmt, rows, cols))
+        want = oracle.dequantize(q, s, fmt, rows, cols)
+        nan = np.isnan(want)
+        np.testing.assert_array_equal(np.isnan(y), nan)
+        np.testing.assert_array_equal(y[~nan].view(np.uint32), want[~nan].view(np.uint32))
