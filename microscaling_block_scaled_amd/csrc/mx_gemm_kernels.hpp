@@ -503,6 +503,20 @@ __device__ __forceinline__ v8i read32(const uint8_t* lb, int toff, int u, int kb
   return v;
 }
 
+// Tile `local` of a rows x cols block of tiles starting at (r0, c0), walked in
+// groups of 4 tile rows so that tiles running together share A and B panels.
+__device__ __forceinline__ void walk_block(int local, int rows, int cols, int r0, int c0, int& tm,
+                                           int& tn) {
+  constexpr int GROUP_M = 4;
+  const int per_group = GROUP_M * cols;
+  const int g = local / per_group;
+  const int first_m = g * GROUP_M;
+  const int gm = rows - first_m < GROUP_M ? rows - first_m : GROUP_M;
+  const int w = local % per_group;
+  tm = r0 + first_m + w % gm;
+  tn = c0 + w / gm;
+}
+
 // Workgroup -> C tile.  Workgroups are dispatched to the 8 XCDs round-robin;
 // give each XCD a contiguous range of tiles, walked in groups of GROUP_M tile
 // rows so that concurrently running tiles share A and B panels in its L2.
@@ -818,6 +832,12 @@ struct FastArgs {
   int64_t ldc;    // fp32 / bf16 C: row pitch in elements
   int tiles_m, tiles_n;
   int vec;        // fp32 / bf16 C: 16 / 8-byte stores allowed (pointer and pitch aligned)
+  // XCD blocks: with part_m * part_n == 8 (and one workgroup per compute unit,
+  // G a multiple of 8), XCD x = b % 8 owns the block (x / part_n, x % part_n) of
+  // a part_m x part_n split of the tile grid and walks it alone, so each XCD's
+  // L2 fetches only its block's A and B panels; 0: one contiguous tile range
+  // per XCD (tile_of)
+  int part_m, part_n;
 };
 
 // Stores of one 32 x 32 accumulator tile acc[i][j] of a wave's 128 x 128 piece
@@ -884,7 +904,11 @@ __global__ __launch_bounds__(256) void k_gemm_fast(FastArgs g) {
   const int nk = (int)(g.K / KS);                // stages per tile (>= NST)
   const int nch = (nk + SPC - 1) / SPC;          // scale chunks per tile
   const int T = g.tiles_m * g.tiles_n, G = gridDim.x, bid = blockIdx.x;
-  const int nt = (T - 1 - bid) / G + 1;          // tiles of this workgroup
+  // tiles of this workgroup: every G-th tile from bid, or every (G / 8)-th
+  // tile of its XCD's block
+  const int bm = g.part_m ? g.tiles_m / g.part_m : 0, bn = g.part_m ? g.tiles_n / g.part_n : 0;
+  const int xcd = bid % 8, wl = bid / 8, wpx = G / 8;
+  const int nt = g.part_m ? (bm * bn - 1 - wl) / wpx + 1 : (T - 1 - bid) / G + 1;
 
   // this wave's panel segments I = wave + 4 k (A segments first, then B);
   // lane chunk I * 64 + lane of the panel, as an offset from the tile's first
@@ -919,7 +943,10 @@ __global__ __launch_bounds__(256) void k_gemm_fast(FastArgs g) {
     TileAt r{(int)M, (int)N};
     if (t < nt) {
       int tm, tn;
-      tile_of(bid + t * G, g.tiles_m, g.tiles_n, tm, tn);
+      if (g.part_m)
+        walk_block(wl + t * wpx, bm, bn, (xcd / g.part_n) * bm, (xcd % g.part_n) * bn, tm, tn);
+      else
+        tile_of(bid + t * G, g.tiles_m, g.tiles_n, tm, tn);
       r.m0 = tm * BM;
       r.n0 = tn * BN;
     }
@@ -1159,6 +1186,22 @@ static hipError_t launch_fast(const GemmCall& gc, int64_t tiles_m, int64_t tiles
   int64_t G = device_cus() & ~7;
   if (G < 8) G = 8;
   if (T < G) G = T;
+  // XCD blocks where the tile grid splits evenly into 8 blocks of at least G / 8
+  // tiles: the split whose blocks need the fewest panel bytes
+  g.part_m = g.part_n = 0;
+  if (G % 8 == 0 && T >= G) {
+    int64_t best = -1;
+    for (int pm = 1; pm <= 8; pm *= 2) {
+      const int pn = 8 / pm;
+      if (tiles_m % pm || tiles_n % pn || (tiles_m / pm) * (tiles_n / pn) < G / 8) continue;
+      const int64_t bytes = (tiles_m / pm) * (gc.K * Fmt<FA>::bits / 8) + (tiles_n / pn) * (gc.K * Fmt<FB>::bits / 8);
+      if (best < 0 || bytes < best) {
+        best = bytes;
+        g.part_m = pm;
+        g.part_n = pn;
+      }
+    }
+  }
   hipLaunchKernelGGL((k_gemm_fast<FA, FB, KS, OUT>), dim3((unsigned)G), dim3(256), 0, gc.st, g);
   return hipGetLastError();
 }
