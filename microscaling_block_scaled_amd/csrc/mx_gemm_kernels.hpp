@@ -156,7 +156,8 @@ __device__ __forceinline__ uint16_t bf16_bits(float a) {
   return __builtin_bit_cast(uint16_t, (__bf16)a);
 }
 
-template <int FA, int FB>
+// BF16OUT: C as bf16 at cb (else fp32 at c); one epilogue per instantiation.
+template <int FA, int FB, bool BF16OUT>
 __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ aq,
                                               const uint8_t* __restrict__ as,
                                               const uint8_t* __restrict__ bq,
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ aq,
       for (int v = 0; v < 4; v++) {
         const int64_t row = m0 + wm * 128 + i * 16 + 4 * kb + v;
         if (row < M && col < N) {
-          if (cb)
+          if (BF16OUT)
             cb[row * ldc + col] = bf16_bits(acc[i][j][v]);
           else
             c[row * ldc + col] = acc[i][j][v];
@@ -275,7 +276,7 @@ __device__ __forceinline__ v8bf i8_bf16(uint2 w, int s) {
 // instruction per 16 x 16 output tile.  Lane l supplies row l % 16 of its
 // operand tile, elements 8 (l / 16) .. 8 (l / 16) + 7 of the block.
 // (a template only so that the units of other formats do not compile it)
-template <int I8 = INT8>
+template <int I8, bool BF16OUT>
 __global__ __launch_bounds__(256) void k_gemm_i8(const uint8_t* __restrict__ aq,
                                                  const uint8_t* __restrict__ as,
                                                  const uint8_t* __restrict__ bq,
@@ -352,7 +353,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(const uint8_t* __restrict__ aq,
       for (int v = 0; v < 4; v++) {
         const int64_t row = m0 + wm * 128 + i * 16 + 4 * kg + v;
         if (row < M && col < N) {
-          if (cb)
+          if (BF16OUT)
             cb[row * ldc + col] = bf16_bits(acc[i][j][v]);
           else
             c[row * ldc + col] = acc[i][j][v];
@@ -368,9 +369,14 @@ static hipError_t gemm_i8_launch(const void* aq, const uint8_t* as, const void* 
                                  int64_t ldc, int out_fmt, uint8_t* out_q, hipStream_t st) {
   if (out_fmt >= 0 && out_fmt != GEMM_OUT_BF16) return hipErrorNotSupported;
   const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  hipLaunchKernelGGL(k_gemm_i8<I8>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st,
-                     (const uint8_t*)aq, as, (const uint8_t*)bq, bs, M, N, K, c,
-                     out_fmt == GEMM_OUT_BF16 ? (uint16_t*)out_q : nullptr, ldc, (int)tiles_n);
+  if (out_fmt == GEMM_OUT_BF16)
+    hipLaunchKernelGGL((k_gemm_i8<I8, true>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st,
+                       (const uint8_t*)aq, as, (const uint8_t*)bq, bs, M, N, K, c, (uint16_t*)out_q, ldc,
+                       (int)tiles_n);
+  else
+    hipLaunchKernelGGL((k_gemm_i8<I8, false>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st,
+                       (const uint8_t*)aq, as, (const uint8_t*)bq, bs, M, N, K, c, nullptr, ldc,
+                       (int)tiles_n);
   return hipGetLastError();
 }
 
@@ -1208,14 +1214,20 @@ static hipError_t launch_fast(const GemmCall& gc, int64_t tiles_m, int64_t tiles
 
 template <int FA, int FB, int KS>
 static hipError_t launch_fast_out(const GemmCall& gc, int64_t tiles_m, int64_t tiles_n) {
-  switch (gc.out_fmt) {
-    case GEMM_OUT_BF16: return launch_fast<FA, FB, KS, OUT_BF16>(gc, tiles_m, tiles_n);
-    case E4M3: return launch_fast<FA, FB, KS, OUT_MX_E4M3>(gc, tiles_m, tiles_n);
-    case E5M2: return launch_fast<FA, FB, KS, OUT_MX_E5M2>(gc, tiles_m, tiles_n);
-    case E2M1: return launch_fast<FA, FB, KS, OUT_MX_E2M1>(gc, tiles_m, tiles_n);
-    default:
-      if (gc.out_fmt >= 0) return hipErrorNotSupported;
-      return launch_fast<FA, FB, KS, OUT_F32>(gc, tiles_m, tiles_n);
+  if constexpr (FA == INT8) {  // MXINT8 products leave as fp32 or bf16 only
+    if (gc.out_fmt == GEMM_OUT_BF16) return launch_fast<FA, FB, KS, OUT_BF16>(gc, tiles_m, tiles_n);
+    if (gc.out_fmt >= 0) return hipErrorNotSupported;
+    return launch_fast<FA, FB, KS, OUT_F32>(gc, tiles_m, tiles_n);
+  } else {
+    switch (gc.out_fmt) {
+      case GEMM_OUT_BF16: return launch_fast<FA, FB, KS, OUT_BF16>(gc, tiles_m, tiles_n);
+      case E4M3: return launch_fast<FA, FB, KS, OUT_MX_E4M3>(gc, tiles_m, tiles_n);
+      case E5M2: return launch_fast<FA, FB, KS, OUT_MX_E5M2>(gc, tiles_m, tiles_n);
+      case E2M1: return launch_fast<FA, FB, KS, OUT_MX_E2M1>(gc, tiles_m, tiles_n);
+      default:
+        if (gc.out_fmt >= 0) return hipErrorNotSupported;
+        return launch_fast<FA, FB, KS, OUT_F32>(gc, tiles_m, tiles_n);
+    }
   }
 }
 
@@ -1245,10 +1257,14 @@ hipError_t gemm_launch(const GemmCall& gc) {
     return gemm_i8_launch<FA>(gc.aq, gc.as, gc.bq, gc.bs, M, N, K, gc.c, gc.ldc, gc.out_fmt, gc.out_q,
                               gc.st);
   } else {
-    hipLaunchKernelGGL((k_gemm<FA, FB>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, gc.st,
-                       (const uint8_t*)gc.aq, gc.as, (const uint8_t*)gc.bq, gc.bs, M, N, K, gc.c,
-                       gc.out_fmt == GEMM_OUT_BF16 ? (uint16_t*)gc.out_q : nullptr, gc.ldc,
-                       (int)tiles_n);
+    if (gc.out_fmt == GEMM_OUT_BF16)
+      hipLaunchKernelGGL((k_gemm<FA, FB, true>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
+                         gc.st, (const uint8_t*)gc.aq, gc.as, (const uint8_t*)gc.bq, gc.bs, M, N, K,
+                         gc.c, (uint16_t*)gc.out_q, gc.ldc, (int)tiles_n);
+    else
+      hipLaunchKernelGGL((k_gemm<FA, FB, false>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
+                         gc.st, (const uint8_t*)gc.aq, gc.as, (const uint8_t*)gc.bq, gc.bs, M, N, K,
+                         gc.c, nullptr, gc.ldc, (int)tiles_n);
     return hipGetLastError();
   }
 }
