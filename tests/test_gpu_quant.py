@@ -5,6 +5,7 @@ import pytest
 import torch
 
 from gpu_util import assert_same_bits, check_guards, dev, guarded_quant_out, host, say
+from sr_ties import sr_tie_tensor, element_codes
 
 pytestmark = pytest.mark.gpu
 
@@ -132,6 +133,23 @@ def test_hadamard_and_sr(mx, oracle, fmt):
     run_both(mx, oracle, d["A"], fmt, 3, 1, True, 0x8421F00D, 42, 5, what="A dual h32 sr signs")
     x32 = (np.random.default_rng(9).standard_normal((64, 96)) * 1e-37).astype(np.float32)
     run_both(mx, oracle, x32, fmt, 3, 0, True, 0x0F0F0F0F, what="f32 tiny h32")
+
+
+@pytest.mark.parametrize("col_blocks", [False, True])
+def test_sr_fraction_ties_with_random_word(mx, oracle, col_blocks):
+    """E2M1 stochastic rounding where the fraction's top 22 bits equal the SR
+    word's: the cases the kernels' hardware conversion cannot decide and must
+    redo with the exact one.  The expected codes follow from the construction
+    and pin the oracle; the GPU must equal the oracle bit for bit."""
+    rows, cols = (256, 64) if col_blocks else (64, 256)
+    seed, off = 0x5EED, 3
+    x, codes, n_up = sr_tie_tensor(oracle, rows, cols, col_blocks, seed, off)
+    assert n_up > 1000  # rounded up by the word's low 10 bits alone
+    lay = 2 if col_blocks else 1
+    want = oracle.quantize(x, 4, lay, 1, 0, seed, off, 0)
+    m = codes >= 0
+    assert np.array_equal(element_codes(want, col_blocks)[m], codes[m])
+    run_both(mx, oracle, x, 4, lay, 1, seed=seed, off=off, what="sr ties")
 
 
 def test_special_blocks(mx, oracle):

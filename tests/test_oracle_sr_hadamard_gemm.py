@@ -121,6 +121,19 @@ def sylvester32():
 C32 = np.float32(1.0 / math.sqrt(32.0))
 
 
+@pytest.mark.parametrize("col_blocks", [False, True])
+def test_sr_decided_by_low_word_bits(oracle, col_blocks):
+    """E2M1 SR on fractions whose top 22 bits equal the SR word's: the low 10
+    bits of the word against the fraction's decide, as the construction says."""
+    from sr_ties import element_codes, sr_tie_tensor
+    rows, cols = (256, 64) if col_blocks else (64, 256)
+    x, codes, n_up = sr_tie_tensor(oracle, rows, cols, col_blocks, 0x5EED, 3)
+    assert n_up > 1000
+    q = oracle.quantize(x, 4, 2 if col_blocks else 1, oracle.SR, 0, 0x5EED, 3, 0)
+    m = codes >= 0
+    assert np.array_equal(element_codes(q, col_blocks)[m], codes[m])
+
+
 def test_hadamard_matrix_identities(oracle):
     H = sylvester32()
     np.testing.assert_array_equal(H @ H.T, 32 * np.eye(32))
