@@ -199,12 +199,15 @@ __device__ __forceinline__ Pack8 int8_convert8(const uint32_t v[8], uint32_t cod
 // fraction has at most 22 bits and the instruction rounds up exactly when
 // r < F (F: the top 32 bits of that fraction); below 1 it compares only the
 // top 22 bits of r and F, so it can differ from the definition only where
-// those agree; and it takes fp32-subnormal inputs at their value instead of as
-// zero.  The second element of a pair takes the seed shifted left by one, so
-// element 2j + 1 gets its result from the pair (2j, 2j + 1) with the seed
-// ~r >> 1.  `redo` is set when an element may be of either kind: a subnormal,
-// or bits 16..31 of r equal to bits 6..21 of floor(|V / X| * 2^23), a
-// superset of the 22-bit agreement.  Such a group takes the exact conversion.
+// those agree.  It takes fp32-subnormal inputs at their value instead of as
+// zero, which matters only for scale codes below 24: from 24 on, a subnormal
+// gives |V / X| < 2^-23, whose top 22 fraction bits are zero, and the
+// instruction returns the signed zero the flush would give.  The second
+// element of a pair takes the seed shifted left by one, so element 2j + 1
+// gets its result from the pair (2j, 2j + 1) with the seed ~r >> 1.  `redo`
+// is set when an element may differ: bits 16..31 of r equal to bits 6..21 of
+// floor(|V / X| * 2^23), a superset of the 22-bit agreement.  Such a group,
+// and every block with a scale code below 24, takes the exact conversion.
 // Only byte 0 of each result is used: the compiler does not carry the
 // instruction's other destination bytes through its first operand.
 typedef float v2f __attribute__((ext_vector_type(2)));
@@ -218,11 +221,11 @@ __device__ __forceinline__ uint32_t sr_fp4_byte(const uint32_t v[8], const uint3
 __device__ __forceinline__ bool sr_fp4_unsure(uint32_t vbits, uint32_t r, int kx) {
   const float f = __builtin_bit_cast(float, vbits);
   const uint32_t key = (uint32_t)__builtin_amdgcn_ldexpf(__builtin_fabsf(f), kx);
-  return ((key & 0xFFFFu) == (r >> 16)) | __builtin_isfpclass(f, 0x90);  // 0x90: +-subnormal
+  return (key & 0xFFFFu) == (r >> 16);
 }
 __device__ __forceinline__ uint32_t sr_fp4_hw8(const uint32_t v[8], uint32_t code, const uint32_t rnd[8],
                                                bool& redo) {
-  const float S = __builtin_bit_cast(float, code << 23);  // 2^(code - 127), code 1 .. 254
+  const float S = __builtin_bit_cast(float, code << 23);  // 2^(code - 127), code 24 .. 254
   const int kx = 144 - (int)code;  // |V| * 2^kx = |V / X| * 2^17, below 2^20
   const uint32_t b0 = sr_fp4_byte<0>(v, rnd, S), b1 = sr_fp4_byte<1>(v, rnd, S);
   const uint32_t b2 = sr_fp4_byte<2>(v, rnd, S), b3 = sr_fp4_byte<3>(v, rnd, S);
@@ -248,7 +251,7 @@ __device__ __forceinline__ Pack8 convert8(const uint32_t v[8], uint32_t code, co
   if (!SR && (F == E4M3 || F == E5M2 || F == E2M1) && code >= (uint32_t)DazFree<F>::value)
     return hw_convert8<F>(v, code);
   if (!SR && F == INT8 && code >= (uint32_t)DazFree<F>::value) return int8_convert8(v, code);
-  if (SR && F == E2M1 && code != 0u) {
+  if (SR && F == E2M1 && code >= 24u) {  // code 0xFF returned above
     bool redo;
     Pack8 o;
     o.w[0] = sr_fp4_hw8(v, code, rnd, redo);

@@ -166,6 +166,13 @@ def test_special_blocks(mx, oracle):
     x[8, 32:64] = np.float32(2.0 ** -126)
     x[9, 64:96] = np.linspace(-448, 448, 32).astype(np.float32)
     x[10, 96:128] = np.float32(6.5)
+    # subnormals beside small normal maxima: E2M1 scale codes 15, 23 and 24 (the
+    # lowest code at which the SR path keeps the hardware conversion)
+    sub = np.array([1e-39, -3e-40, 5e-41, -1.1e-38, 7e-39, -2e-45, 1.17e-38, -9e-39], np.float32)
+    for row, e in ((11, -110), (12, -102), (13, -101)):
+        x[row, 128:160] = np.tile(sub, 4)
+        x[row, 128] = np.float32(2.0 ** e)
+        x[row, 131] = np.float32(-1.5 * 2.0 ** (e - 1))
     for fmt in range(6):
         for lay in (1, 2, 3):
             run_both(mx, oracle, x, fmt, lay, 0, what="special")
