@@ -247,15 +247,16 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ aq,
 // gfx950's block-scaled matrix instruction takes no integer elements.  An
 // MXINT8 element n / 64 times its block scale 2^(s - 127) is n * 2^(s - 133):
 // an integer of at most 7 significant bits times a power of two, which bf16
-// holds exactly (8 significant bits) wherever the result is a normal number.
+// holds exactly (8 significant bits) at or above 2^-126; below that (scale
+// codes under 7) it is a multiple of 2^-133, bf16's subnormal step, so it is
+// exact as a subnormal.  The conversion and the bf16 instruction keep
+// subnormals, so every product is exact whatever the other operand's scale.
 // So each lane turns its operand bytes into bf16 with the scale folded in, and
 // a bf16 matrix instruction with K = 32 -- one block per instruction -- forms
 // the products exactly and accumulates them in fp32.  Folding the scale into
 // the operands costs one conversion per operand element per tile pass; an
 // integer instruction would instead need a per-output fp32 rescale after every
-// block, which the vector ALU cannot keep up with.  Values of blocks with scale
-// codes below 7 fall below bf16's normal range and round; their contribution
-// is below 2^-120 per product.
+// block, which the vector ALU cannot keep up with.
 // 8 INT8 codes (w: bytes 0..7 = elements 0..7) of one block with scale code
 // s, as bf16 values n * 2^(s - 133).
 __device__ __forceinline__ v8bf i8_bf16(uint2 w, int s) {
