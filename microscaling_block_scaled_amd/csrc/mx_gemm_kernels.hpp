@@ -558,7 +558,9 @@ struct Lanes {
 
 // The scale bytes of one stage for the wave's 8 tiles: KS / 32 bytes per row
 // (one or two dwords), read once per stage from chunk buffer `par` at byte
-// offset `off` of each row's 32.
+// offset `off` of each row's 32.  A chunk buffer holds blocks of 32 rows, each
+// as [16-byte half][row][16 bytes], so the 32 rows a read takes sit 16 bytes
+// apart (two rows to a bank) instead of 32.
 template <int KS> struct ScaleWords {
   uint32_t a[4][KS / 128], b[4][KS / 128];
 };
@@ -566,11 +568,13 @@ template <int KS> struct ScaleWords {
 template <class C>
 __device__ __forceinline__ void read_scale_words(ScaleWords<C::KS>& sw, const uint8_t* lds, int par,
                                                  int off, const Lanes& w) {
-  const uint8_t* sc = lds + C::SC_OFF + par * C::SC_BUF + off;
+  const uint8_t* sc = lds + C::SC_OFF + par * C::SC_BUF + (off >> 4) * 512 + (off & 15);
+  const uint8_t* sa = sc + (w.arow >> 5) * 1024 + (w.arow & 31) * 16;
+  const uint8_t* sb = sc + (8 + (w.brow >> 5)) * 1024 + (w.brow & 31) * 16;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    const uint8_t* pa = sc + (w.arow + 32 * i) * C::SC_ROW;
-    const uint8_t* pb = sc + (256 + w.brow + 32 * i) * C::SC_ROW;
+    const uint8_t* pa = sa + 1024 * i;
+    const uint8_t* pb = sb + 1024 * i;
     if (C::KS == 256) {
       const uint2 x = *(const uint2*)pa, y = *(const uint2*)pb;
       sw.a[i][0] = x.x; sw.a[i][C::KS / 128 - 1] = x.y;
@@ -936,9 +940,9 @@ __global__ __launch_bounds__(256) void k_gemm_fast(FastArgs g) {
     lofs[k] = (uint32_t)((isb[k] ? C::B_OFF : C::A_OFF) + Ip * 1024);
   }
   // scale chunks: wave w loads A scale rows 64 w .. 64 w + 63 and the same B
-  // rows, 32 rows per load, lane pair (2 r, 2 r + 1) the two 16-byte halves of
-  // row r's 32 bytes
-  const uint32_t vs0 = (uint32_t)(wave * 64 + (lane >> 1)) * nblk + 16 * (lane & 1);
+  // rows, 32 rows per load; lane l takes 16-byte half l / 32 of row l % 32, so
+  // a 32-row block lands in LDS as [half][row][16 bytes] (read_scale_words)
+  const uint32_t vs0 = (uint32_t)(wave * 64 + (lane & 31)) * nblk + 16 * (lane >> 5);
   const uint32_t vs1 = vs0 + 32 * nblk;
   const uint32_t lds0 = lds_addr(lds);
   const v4i rnone = {0, 0, 0, 0x00020000};
