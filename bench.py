@@ -27,6 +27,7 @@ METRIC = "MX quantize GB/s + MX-GEMM TFLOPS (MXFP8/MXFP4), % of HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0
 PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0, "fp6": 10100.0, "bf16": 2500.0}
 M, N, K = 8192, 4096, 14336
+SAMPLE_A, SAMPLE_W = 1024, 384  # rows of A and W the CPU oracle repeats
 
 
 def dev_bf16(a):
@@ -76,6 +77,7 @@ def bench_step(mx, steps, warmup):
     from microscaling_block_scaled_amd.synth import make
     d = make("mxfp4_mlp")
     a, w = dev_bf16(d["A"]), dev_bf16(d["W"])
+    sample = {"A": d["A"][:SAMPLE_A].copy(), "W": d["W"][:SAMPLE_W].copy()}
     del d
     st = torch.cuda.current_stream()
     oa = mx.quantize(a, mx.E2M1, mx.LAYOUT_ROW, mx.SR, True, 0, 42, 0)
@@ -111,8 +113,13 @@ def bench_step(mx, steps, warmup):
     settle(lambda: (quant_w(), quant_a()))
     qa, _ = timed_events(quant_a, 20, st)
     qw, _ = timed_events(quant_w, 20, st)
+    step()  # the outputs of one more step, for the parity check against the oracle's sample
+    torch.cuda.synchronize()
+    sample["gpu"] = {"qa": oa["q_row"][:SAMPLE_A].cpu().numpy(), "sa": oa["s_row"][:SAMPLE_A].cpu().numpy(),
+                     "qw": ow["q_row"][:SAMPLE_W].cpu().numpy(), "sw": ow["s_row"][:SAMPLE_W].cpu().numpy(),
+                     "c": c[:SAMPLE_A, :SAMPLE_W].cpu().numpy()}
     return {"ms_per_step": wall * 1e3 / steps, "quant_a_ms": qa, "quant_w_ms": qw,
-            "gemm_ms": sum(gm) / len(gm), "gemm_ms_median": gm[steps // 2]}
+            "gemm_ms": sum(gm) / len(gm), "gemm_ms_median": gm[steps // 2], "sample": sample}
 
 
 def bench_quant(mx, name, x_host, fmt, layouts, rounds=100):
@@ -211,28 +218,41 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
-def cpu_baseline():
+def cpu_baseline(sample):
     """The CPU oracle (test infrastructure, untuned), timed on bounded samples
     of the same workloads on this host's cores:
-      - the step: quantize 1024 rows of A (H32 + SR), 384 rows of W (H32 +
-        RNE) and the 1024 x 384 fp64 dot products of their MX values, scaled
-        to the full step (the headline value, all threads);
+      - the step: quantize the first 1024 rows of A (H32 + SR) and 384 rows of
+        W (H32 + RNE) of the benchmark's own inputs, and the 1024 x 384 fp64 dot
+        products of their MX values, scaled to the full step (the headline
+        value, all threads);
       - quantize GB/s (same algorithmic-bytes formula as the GPU figures) on
         512-row samples of the 4096^2 sweep (every format and layout) and of
-        the dual-layout tensor, on all threads and on one."""
+        the dual-layout tensor, on all threads and on one.
+    Afterwards (untimed) the same rows and block of the GPU step's outputs are
+    compared with the oracle's: codes and scales bit for bit, C within
+    1e-5 * sum|a*b| + 2^-126."""
+    import numpy as np
     import oracle
     from microscaling_block_scaled_amd.synth import make
     threads = oracle.set_threads(0)
-    ra, rw = 1024, 384
-    d = make("mxfp4_mlp", {"A": (ra, K), "W": (rw, K)})
+    ra, rw = SAMPLE_A, SAMPLE_W
     t0 = time.perf_counter()
-    qa = oracle.quantize(d["A"], oracle.E2M1, 1, oracle.SR, oracle.FLAG_HADAMARD32, 42)
+    qa = oracle.quantize(sample["A"], oracle.E2M1, 1, oracle.SR, oracle.FLAG_HADAMARD32, 42)
     t1 = time.perf_counter()
-    qw = oracle.quantize(d["W"], oracle.E2M1, 1, oracle.RNE, oracle.FLAG_HADAMARD32)
+    qw = oracle.quantize(sample["W"], oracle.E2M1, 1, oracle.RNE, oracle.FLAG_HADAMARD32)
     t2 = time.perf_counter()
-    oracle.gemm_f64(qa["q_row"], qa["s_row"], 4, qw["q_row"], qw["s_row"], 4, ra, rw, K)
+    c_ref, t_ref = oracle.gemm_f64(qa["q_row"], qa["s_row"], 4, qw["q_row"], qw["s_row"], 4, ra, rw, K)
     t3 = time.perf_counter()
     full = (t1 - t0) * (M / ra) + (t2 - t1) * (N / rw) + (t3 - t2) * (M * N / (ra * rw))
+    g = sample["gpu"]
+    ratio = np.abs(g["c"].astype(np.float64) - c_ref) / (1e-5 * t_ref + 2.0 ** -126)
+    parity = {
+        "sample": f"rows 0..{ra - 1} of A, rows 0..{rw - 1} of W and C[0:{ra}, 0:{rw}] of the timed step",
+        "quant_a_bit_exact": bool(np.array_equal(g["qa"], qa["q_row"]) and np.array_equal(g["sa"], qa["s_row"])),
+        "quant_w_bit_exact": bool(np.array_equal(g["qw"], qw["q_row"]) and np.array_equal(g["sw"], qw["s_row"])),
+        "gemm_worst_err_over_bound": float(np.nanmax(ratio)),
+        "gemm_elements_over_bound": int((~(ratio <= 1.0)).sum()),
+    }
 
     def q_gbs(x, fmt, lay, n_threads):
         oracle.set_threads(n_threads)
@@ -259,7 +279,7 @@ def cpu_baseline():
                       f"({t3 - t0:.1f} s), scaled to the full step ({full:.0f} s)",
             "cpu_model": cpu_model(), "logical_cpus": os.cpu_count(),
             "quantize": {"sample": "512 rows x 4096 of the sweep and of the dual-layout tensor",
-                         **quant}}
+                         **quant}}, parity
 
 
 GEMM_KERNEL = "void mx::k_gemm_fast<4, 4, 256, 0>"
@@ -385,7 +405,7 @@ def main():
         ks["linear_step_mxfp8"] = bench_linear(mx, mx.E4M3, PEAK_TFLOPS["fp8"])
         out["kernels"] = ks
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline()
+        out["cpu_baseline"], out["parity"] = cpu_baseline(res["sample"])
     print(json.dumps(out))
 
 
