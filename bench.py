@@ -148,6 +148,23 @@ def bench_quant(mx, name, x_host, fmt, layouts, rounds=100):
             "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def bench_copy(name, nbytes, rounds=100):
+    """A plain device-to-device copy of `nbytes` (read nbytes, write nbytes) over
+    rotating buffer sets (>= 1 GiB), timed like the quantizers: the floor that
+    memory traffic of that size reaches on this GPU."""
+    import torch
+    nsets = max(2, int((1 << 30) // (2 * nbytes)) + 1)
+    src = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(nsets)]
+    dst = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(nsets)]
+    st = torch.cuda.current_stream()
+    med, _ = timed_events(lambda i: dst[i % nsets].copy_(src[i % nsets]), max(rounds // 5, 4), st)
+    gbs = 2 * nbytes / (med * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"workload": name, "bytes": 2 * nbytes, "ms": round(med, 5), "GB/s": round(gbs, 1),
+            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def bench_gemm(mx, name, a_host, w_host, fa, fw, peak, rounds=100, out_fmt=None):
     """One product timed alone; with ``out_fmt`` the product leaves the kernel
     in that MX format (mx_gemm_mx) instead of fp32."""
@@ -377,6 +394,12 @@ def main():
                 ks[f"sweep_{fname}_{lname}"] = bench_quant(
                     mx, f"bf16 [4096x4096] -> {fname} {lname}", x, f, lay)
         del x
+        # memory-only floors of the same sizes: a copy of the sweep's bf16 input and of the
+        # dual-layout one
+        ks["copy_floor_4096x4096_bf16"] = bench_copy("device copy of 32 MiB (the sweep input)",
+                                                     4096 * 4096 * 2)
+        ks["copy_floor_16384x4096_bf16"] = bench_copy("device copy of 128 MiB (the dual-layout input)",
+                                                      16384 * 4096 * 2)
         d = make("mxfp8_mlp")
         ks["gemm_mxfp8_mlp"] = bench_gemm(mx, "E4M3 M=8192 N=14336 K=4096", d["A"], d["W"],
                                           mx.E4M3, mx.E4M3, PEAK_TFLOPS["fp8"])
