@@ -297,6 +297,35 @@ def test_full_size_gemm_sampled(mx, oracle, case):
     assert_gemm_close(cs, cref, t, case)
 
 
+@pytest.mark.parametrize("fa,fb,M,N,K", [(4, 4, 40 * 256 - 37, 16 * 256 - 5, 512),
+                                         (0, 0, 33 * 256 + 100, 9 * 256 + 17, 1536)])
+def test_staged_uneven_tiles(mx, oracle, fa, fb, M, N, K):
+    """The persistent staged kernel with more tiles than workgroups and an
+    uneven share per workgroup, ragged in M and N: 40 x 16 tiles (the tile
+    grid splits into 8 XCD blocks of 10 x 8; 2.5 tiles per workgroup) and
+    34 x 10 tiles (no even split: one contiguous range per XCD).  C sits in a
+    guard band; every position of the 256 x 256 tile is checked at the plain
+    bound."""
+    rng = np.random.default_rng(M + N)
+    from microscaling_block_scaled_amd.synth import bf16_bits
+    a = bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    (ga, oa), (gw, ow) = quant_pair(mx, oracle, a, w, fa, fb)
+    del a, w
+    say("gemm uneven tiles", M, N, K, FMT_NAMES[fa], FMT_NAMES[fb])
+    c = Guarded((M, N), torch.float32)
+    mx.gemm(ga["q_row"], ga["s_row"], fa, gw["q_row"], gw["s_row"], fb, M, N, K, c=c.t)
+    torch.cuda.synchronize()
+    c.check("C")
+    ms, ns = tile_positions(M, N, 7)
+    cs = host(c.t[torch.from_numpy(ms).cuda(), torch.from_numpy(ns).cuda()])
+    cref, t = oracle.gemm_f64_at(oa["q_row"], oa["s_row"], fa, ow["q_row"], ow["s_row"], fb,
+                                 M, N, K, ms, ns)
+    worst, over, rel = gemm_report(cs, cref, t)
+    print(f"uneven {M}x{N}x{K}: worst |err|/sum|ab| = {rel:.3g} ({worst:.3g} of the bound), {over} over")
+    assert_gemm_close(cs, cref, t, "uneven tiles")
+
+
 # ---------------------------------------------------------------------------
 # partial blocks along K: the operands hold K padded to whole blocks
 # ---------------------------------------------------------------------------
