@@ -353,16 +353,19 @@ __global__ __launch_bounds__(256) void k_quant_blocks(QP p) {
     am = umax(m << 16, m & 0xFFFF0000u);
   } else {
     // Flush subnormal inputs before the transform.  For bf16 a block is first
-    // checked on the packed pairs (magnitude - 1 wraps for zero, lands below
-    // 0x7F only for a subnormal), and only lanes holding one flush.
+    // checked on the packed pairs: per half, 2 h - 2 (mod 2^16) drops the sign
+    // bit, wraps zero to 0xFFFE and lands below 0xFD only for a subnormal (one
+    // packed multiply-add); only lanes holding one flush.
     bool sub = true;
     if constexpr (SRC == SRC_BF16 && HAD) {
       u16x2 mn = {0xFFFF, 0xFFFF};
-      const u16x2 one = {1, 1};
 #pragma unroll
-      for (int i = 0; i < 16; i++)
-        mn = __builtin_elementwise_min(mn, __builtin_bit_cast(u16x2, raw[i] & 0x7FFF7FFFu) - one);
-      sub = mn.x < 0x7F || mn.y < 0x7F;
+      for (int i = 0; i < 16; i++) {
+        uint32_t t;  // per half: h * 2 + 0xFFFE (the compiler would split it in two)
+        asm("v_pk_mad_u16 %0, %1, 2, -2" : "=v"(t) : "v"(raw[i]));
+        mn = __builtin_elementwise_min(mn, __builtin_bit_cast(u16x2, t));
+      }
+      sub = mn.x < 0xFD || mn.y < 0xFD;
     }
 #pragma unroll
     for (int j = 0; j < 4; j++) widen8<SRC>(&raw[j * 2 * ESZ], &v[8 * j]);

@@ -92,6 +92,11 @@ def test_exhaustive_bf16_patterns(mx, oracle, fmt):
         run_both(mx, oracle, x, fmt, 1, rnd, seed=123456789, off=3, what="exhaustive rows")
     run_both(mx, oracle, x, fmt, 2, 0, what="exhaustive cols")
     run_both(mx, oracle, x, fmt, 3, 0, what="exhaustive dual")
+    # the transform after the flush of bf16 subnormal inputs (every pattern is in
+    # some block), with and without a sign mask and SR
+    run_both(mx, oracle, x, fmt, 1, 0, True, 0, what="exhaustive rows h32")
+    run_both(mx, oracle, x, fmt, 1, 1, True, 0x5A5A5A5A, 7, 1, what="exhaustive rows h32 sr signs")
+    run_both(mx, oracle, x, fmt, 2, 0, True, 0, what="exhaustive cols h32")
 
 
 def test_dual_layout_e4m3(mx, oracle):
