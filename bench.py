@@ -299,7 +299,7 @@ def cpu_baseline(sample):
                          **quant}}, parity
 
 
-GEMM_KERNEL = "void mx::k_gemm_fast<4, 4, 256, 0>"
+GEMM_KERNEL = "void mx::k_gemm_fast<4, 4, 256, 0, true>"
 
 
 def load_traffic(src_hash):

@@ -438,6 +438,9 @@ template <int FA, int FB, int KS_> struct Fast {
   static constexpr int SC_OFF = NST * STAGE;
   static constexpr int TOTAL = SC_OFF + 2 * SC_BUF;
   static_assert(NST >= 2 && SPC >= NST, "stage ring and scale buffers");
+  // spread scale loads: the last of a chunk's four must land before its first
+  // stage
+  static_assert(SPC % 4 == 0 && NST - 1 <= SPC / 4, "spread scale loads");
 };
 
 template <int CH>
@@ -893,7 +896,7 @@ __device__ __forceinline__ void store_tile(const v16f& t, const FastArgs& g, int
   }
 }
 
-template <int FA, int FB, int KS, int OUT>
+template <int FA, int FB, int KS, int OUT, bool SPREAD>
 __global__ __launch_bounds__(256) void k_gemm_fast(FastArgs g) {
   using C = Fast<FA, FB, KS>;
   constexpr int NST = C::NST, SUB = C::SUB, SPC = C::SPC;
@@ -977,23 +980,58 @@ __global__ __launch_bounds__(256) void k_gemm_fast(FastArgs g) {
     return r;
   };
   // Load j (0 .. NLD-1) of stage sl of the tile with resources r, into ring
-  // slot `slot`: the four scale loads (masked off except at the first stage
-  // of a chunk, so the loop body has no branch; chunk buffers alternate with
-  // the workgroup's running chunk count, parity `par`), then the panel
-  // segments.
-  constexpr int NLD = 4 + SEGS;
+  // slot `slot`: with SPREAD, j = 0 is no load here (the scale piece of the
+  // stage, scale_piece); else the four scale loads of a chunk (masked off
+  // except at the first stage of a chunk, so the loop body has no branch;
+  // chunk buffers alternate with the workgroup's running chunk count, parity
+  // `par`).  Then the panel segments.
+  constexpr int NSC = SPREAD ? 1 : 4;
+  constexpr int NLD = NSC + SEGS;
   auto issue_one = [&](const TileRs& r, int sl, int par, int slot, int j) {
-    if (j < 4) {
-      const bool chunk = (sl % SPC) == 0;
-      const uint32_t sdst = lds0 + C::SC_OFF + par * C::SC_BUF + wave * 64 * C::SC_ROW +
-                            (j >> 1) * 256 * C::SC_ROW + (j & 1) * 32 * C::SC_ROW;
-      const uint32_t vo = ((j & 1) ? vs1 : vs0) + (uint32_t)(sl / SPC) * C::SC_ROW;
-      dma16_if(j < 2 ? r.sa : r.sb, vo, 0u, sdst, chunk);
+    if (j < NSC) {
+      if constexpr (!SPREAD) {
+        const bool chunk = (sl % SPC) == 0;
+        const uint32_t sdst = lds0 + C::SC_OFF + par * C::SC_BUF + wave * 64 * C::SC_ROW +
+                              (j >> 1) * 256 * C::SC_ROW + (j & 1) * 32 * C::SC_ROW;
+        const uint32_t vo = ((j & 1) ? vs1 : vs0) + (uint32_t)(sl / SPC) * C::SC_ROW;
+        dma16_if(j < 2 ? r.sa : r.sb, vo, 0u, sdst, chunk);
+      }
     } else {
-      const int k = j - 4;
+      const int k = j - NSC;
       dma16(isb[k] ? r.b : r.a, voff[k], (uint32_t)sl * (isb[k] ? C::RBB : C::RBA),
             lds0 + (uint32_t)(slot * C::STAGE) + lofs[k]);
     }
+  };
+  // SPREAD (every chunk of every tile whole, at least two chunks per tile):
+  // the four loads of a chunk, one per stage, SPC / 4 stages apart.  Counting
+  // the chunks of the workgroup's tiles in order (chunk c in buffer c & 1),
+  // load q of chunk c (A rows, then B rows; 32 rows each, then the next 32)
+  // rides with the panel loads issued during stage SPC (c - 1) - 1 + q SPC / 4,
+  // stages counted the same way: by then every wave has read its last scale
+  // words of chunk c - 2 from that buffer (at that stage's barrier), and the
+  // last load lands by the wait before chunk c's first stage, whose words are
+  // read just after it (NST - 1 <= SPC / 4).  Seen from tile t, the piece
+  // issued during its stage s (s < 0: the prologue, which loads chunk 0 whole
+  // before) belongs to chunk cc = floor((s + 1) / SPC) + 1 of the stream of
+  // chunks from tile t on: a chunk of tile t or t + 1.
+  auto scale_piece = [&](int t, int s, TileAt a0, TileAt a1) {
+    constexpr int GAP = SPC / 4;
+    const int d = s + 1;  // >= 1 - NST >= -SPC
+    const int fl = d < 0 ? -1 : d / SPC;
+    const int pos = d - fl * SPC, cc = fl + 1, q = pos / GAP;
+    int c = cc;
+    TileAt a = a0;
+    if (c >= nch) {
+      c -= nch;
+      a = a1;
+    }
+    const bool bpart = q >= 2;
+    const uint32_t rows = (uint32_t)(bpart ? N - a.n0 : M - a.m0);
+    const v4i rs = make_rsrc((bpart ? g.bs + (int64_t)a.n0 * nblk : g.as + (int64_t)a.m0 * nblk), rows * nblk);
+    const uint32_t dst = lds0 + C::SC_OFF + ((t * nch + cc) & 1) * C::SC_BUF + wave * 64 * C::SC_ROW +
+                         (q >> 1) * 256 * C::SC_ROW + (q & 1) * 32 * C::SC_ROW;
+    const uint32_t vo = ((q & 1) ? vs1 : vs0) + (uint32_t)c * C::SC_ROW;
+    dma16_if(rs, vo, 0u, dst, cc > 0 && pos % GAP == 0);
   };
 
   Lanes w;
@@ -1029,10 +1067,19 @@ __global__ __launch_bounds__(256) void k_gemm_fast(FastArgs g) {
   // (a wait counts panel loads only: masked-off scale loads may or may not
   // count, and where they do the wait is merely longer), then the operands of
   // its first RA substeps
+  if constexpr (SPREAD) {
+    const TileRs r0 = tile_rs(cur);
 #pragma unroll
-  for (int i = 0; i < NST; i++)
+    for (int j = 0; j < 4; j++)
+      dma16(j < 2 ? r0.sa : r0.sb, (j & 1) ? vs1 : vs0, 0u,
+            lds0 + C::SC_OFF + wave * 64 * C::SC_ROW + (j >> 1) * 256 * C::SC_ROW + (j & 1) * 32 * C::SC_ROW);
+  }
+#pragma unroll
+  for (int i = 0; i < NST; i++) {
+    if constexpr (SPREAD) scale_piece(0, i - NST, cur, nxt);
 #pragma unroll
     for (int j = 0; j < NLD; j++) issue_one(tile_rs(cur), i, (i / SPC) & 1, i, j);
+  }
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"((NST - 1) * SEGS) : "memory");
   __builtin_amdgcn_sched_barrier(0);
@@ -1098,7 +1145,12 @@ __global__ __launch_bounds__(256) void k_gemm_fast(FastArgs g) {
         if constexpr (gi >= 0 && gi < NSLOT) {
           static_for<NLD>([&](auto J) {
             constexpr int j = decltype(J)::value;
-            if constexpr ((j * NSLOT) / NLD == gi) issue_one(lr, sl, lpar, cslot, j);
+            if constexpr ((j * NSLOT) / NLD == gi) {
+              if constexpr (SPREAD && j == 0)
+                scale_piece(t, s, cur, nxt);
+              else
+                issue_one(lr, sl, lpar, cslot, j);
+            }
           });
         }
       };
@@ -1165,7 +1217,7 @@ inline int device_cus() {
   return n;
 }
 
-template <int FA, int FB, int KS, int OUT>
+template <int FA, int FB, int KS, int OUT, bool SPREAD = false>
 static hipError_t launch_fast(const GemmCall& gc, int64_t tiles_m, int64_t tiles_n) {
   FastArgs g;
   g.aq = (const uint8_t*)gc.aq;
@@ -1213,25 +1265,29 @@ static hipError_t launch_fast(const GemmCall& gc, int64_t tiles_m, int64_t tiles
       }
     }
   }
-  hipLaunchKernelGGL((k_gemm_fast<FA, FB, KS, OUT>), dim3((unsigned)G), dim3(256), 0, gc.st, g);
+  hipLaunchKernelGGL((k_gemm_fast<FA, FB, KS, OUT, SPREAD>), dim3((unsigned)G), dim3(256), 0, gc.st, g);
   return hipGetLastError();
 }
 
+// fp32 and bf16 output spread each scale chunk's loads over its stages where
+// every chunk is whole and a tile has at least two (K % 1024 == 0, K >= 2048)
 template <int FA, int FB, int KS>
 static hipError_t launch_fast_out(const GemmCall& gc, int64_t tiles_m, int64_t tiles_n) {
+  const bool spread = gc.K % 1024 == 0 && gc.K >= 2048;
+  if (gc.out_fmt == GEMM_OUT_BF16)
+    return spread ? launch_fast<FA, FB, KS, OUT_BF16, true>(gc, tiles_m, tiles_n)
+                  : launch_fast<FA, FB, KS, OUT_BF16>(gc, tiles_m, tiles_n);
+  if (gc.out_fmt < 0)
+    return spread ? launch_fast<FA, FB, KS, OUT_F32, true>(gc, tiles_m, tiles_n)
+                  : launch_fast<FA, FB, KS, OUT_F32>(gc, tiles_m, tiles_n);
   if constexpr (FA == INT8) {  // MXINT8 products leave as fp32 or bf16 only
-    if (gc.out_fmt == GEMM_OUT_BF16) return launch_fast<FA, FB, KS, OUT_BF16>(gc, tiles_m, tiles_n);
-    if (gc.out_fmt >= 0) return hipErrorNotSupported;
-    return launch_fast<FA, FB, KS, OUT_F32>(gc, tiles_m, tiles_n);
+    return hipErrorNotSupported;
   } else {
     switch (gc.out_fmt) {
-      case GEMM_OUT_BF16: return launch_fast<FA, FB, KS, OUT_BF16>(gc, tiles_m, tiles_n);
       case E4M3: return launch_fast<FA, FB, KS, OUT_MX_E4M3>(gc, tiles_m, tiles_n);
       case E5M2: return launch_fast<FA, FB, KS, OUT_MX_E5M2>(gc, tiles_m, tiles_n);
       case E2M1: return launch_fast<FA, FB, KS, OUT_MX_E2M1>(gc, tiles_m, tiles_n);
-      default:
-        if (gc.out_fmt >= 0) return hipErrorNotSupported;
-        return launch_fast<FA, FB, KS, OUT_F32>(gc, tiles_m, tiles_n);
+      default: return hipErrorNotSupported;
     }
   }
 }

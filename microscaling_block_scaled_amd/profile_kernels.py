@@ -234,13 +234,14 @@ def _counter_table(d: str):
 
 
 GEMM_FLOPS = {  # 2 M N K of the products the driver runs, by kernel template arguments
-    "k_gemm_fast<4, 4, 256, 0>": (2.0 * 8192 * 4096 * 14336, 10100.0, "MXFP4 8192x4096x14336"),
-    "k_gemm_fast<0, 0, 128, 0>": (2.0 * 8192 * 14336 * 4096, 5000.0, "MXFP8 E4M3 8192x14336x4096"),
-    "k_gemm_fast<0, 0, 128, 2>": (2.0 * 8192 * 14336 * 4096, 5000.0, "MXFP8 E4M3, E4M3 MX output"),
-    "k_gemm_fast<1, 0, 128, 0>": (2.0 * 4096 * 4096 * 14336, 5000.0, "MXFP8 E5M2 x E4M3 4096x4096x14336"),
-    "k_gemm_fast<2, 2, 128, 0>": (2.0 * 8192 * 4096 * 14336, 10100.0, "MXFP6 E2M3 8192x4096x14336"),
-    "k_gemm_fast<2, 4, 128, 0>": (2.0 * 8192 * 4096 * 14336, 10100.0, "E2M3 x E2M1 8192x4096x14336"),
-    "k_gemm_fast<5, 5, 128, 0>": (2.0 * 8192 * 14336 * 4096, 2500.0, "MXINT8 (bf16 instruction) 8192x14336x4096"),
+    # (FA, FB, KS, output kind, scale loads spread over a chunk's stages)
+    "k_gemm_fast<4, 4, 256, 0, true>": (2.0 * 8192 * 4096 * 14336, 10100.0, "MXFP4 8192x4096x14336"),
+    "k_gemm_fast<0, 0, 128, 0, true>": (2.0 * 8192 * 14336 * 4096, 5000.0, "MXFP8 E4M3 8192x14336x4096"),
+    "k_gemm_fast<0, 0, 128, 2, false>": (2.0 * 8192 * 14336 * 4096, 5000.0, "MXFP8 E4M3, E4M3 MX output"),
+    "k_gemm_fast<1, 0, 128, 0, true>": (2.0 * 4096 * 4096 * 14336, 5000.0, "MXFP8 E5M2 x E4M3 4096x4096x14336"),
+    "k_gemm_fast<2, 2, 128, 0, true>": (2.0 * 8192 * 4096 * 14336, 10100.0, "MXFP6 E2M3 8192x4096x14336"),
+    "k_gemm_fast<2, 4, 128, 0, true>": (2.0 * 8192 * 4096 * 14336, 10100.0, "E2M3 x E2M1 8192x4096x14336"),
+    "k_gemm_fast<5, 5, 128, 0, true>": (2.0 * 8192 * 14336 * 4096, 2500.0, "MXINT8 (bf16 instruction) 8192x14336x4096"),
 }
 N_SIMD, N_XCD, NOMINAL_GHZ = 1024, 8, 2.4
 

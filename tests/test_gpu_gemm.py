@@ -166,7 +166,7 @@ def test_mxint8_gemm(mx, oracle):
     differ widely; the products are exact, so the plain tolerance holds."""
     rng = np.random.default_rng(77)
     from microscaling_block_scaled_amd.synth import bf16_bits
-    for (M, N, K) in [(288, 320, 1536), (100, 36, 608), (16, 16, 32)]:
+    for (M, N, K) in [(288, 320, 1536), (300, 520, 2048), (100, 36, 608), (16, 16, 32)]:
         a = rng.standard_normal((M, K)) * np.exp2(rng.integers(-40, 41, (M, 1)))
         a = bf16_bits(a.astype(np.float32))
         w = bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
@@ -298,12 +298,17 @@ def test_full_size_gemm_sampled(mx, oracle, case):
 
 
 @pytest.mark.parametrize("fa,fb,M,N,K", [(4, 4, 40 * 256 - 37, 16 * 256 - 5, 512),
-                                         (0, 0, 33 * 256 + 100, 9 * 256 + 17, 1536)])
+                                         (0, 0, 33 * 256 + 100, 9 * 256 + 17, 1536),
+                                         (4, 4, 40 * 256 - 37, 16 * 256 - 5, 2048),
+                                         (0, 0, 33 * 256 + 100, 9 * 256 + 17, 3072)])
 def test_staged_uneven_tiles(mx, oracle, fa, fb, M, N, K):
     """The persistent staged kernel with more tiles than workgroups and an
     uneven share per workgroup, ragged in M and N: 40 x 16 tiles (the tile
     grid splits into 8 XCD blocks of 10 x 8; 2.5 tiles per workgroup) and
-    34 x 10 tiles (no even split: one contiguous range per XCD).  C sits in a
+    34 x 10 tiles (no even split: one contiguous range per XCD).  K = 512 and
+    1536 load each scale chunk at its first stage; K = 2048 and 3072 (two and
+    three whole chunks of 1024 per tile) spread a chunk's loads over its
+    stages, so chunks of the next tile load while this one runs.  C sits in a
     guard band; every position of the 256 x 256 tile is checked at the plain
     bound."""
     rng = np.random.default_rng(M + N)

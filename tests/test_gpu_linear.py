@@ -30,7 +30,8 @@ def test_gemm_bf16_is_rounded_fp32(mx, oracle, fa, fb):
     2^60 so that rounding carries, large and small magnitudes all occur."""
     rng = np.random.default_rng(31 + fa)
     from microscaling_block_scaled_amd.synth import bf16_bits
-    for (M, N, K, ldc) in [(288, 320, 1024, 320), (100, 36, 512, 40), (70, 48, 96, 52)]:
+    for (M, N, K, ldc) in [(288, 320, 1024, 320), (300, 260, 2048, 264), (100, 36, 512, 40),
+                           (70, 48, 96, 52)]:
         a = rng.standard_normal((M, K)) * np.exp2(rng.integers(-30, 31, (M, 1)))
         w = rng.standard_normal((N, K)) * np.exp2(rng.integers(-30, 31, (N, 1)))
         (ga, _), (gw, _) = quant_pair(mx, oracle, bf16_bits(a.astype(np.float32)),
