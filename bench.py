@@ -36,6 +36,50 @@ def dev_bf16(a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
 
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence:
+    recording it on a stream issues no system-scope release (no cache
+    writeback and invalidate between the kernels it brackets), so the kernels
+    of a step run back to back as they do without events.  The HIP runtime is
+    the one torch has loaded (soname libamdhip64.so.7)."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        if TimingEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so.7")
+            for fn, args in (("hipEventCreateWithFlags", [ctypes.c_void_p, ctypes.c_uint]),
+                             ("hipEventRecord", [ctypes.c_void_p, ctypes.c_void_p]),
+                             ("hipEventElapsedTime", [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+                             ("hipEventDestroy", [ctypes.c_void_p])):
+                getattr(hip, fn).argtypes = args
+                getattr(hip, fn).restype = ctypes.c_int
+            TimingEvent._hip = hip
+        self._ev = ctypes.c_void_p()
+        self._check(self._hip.hipEventCreateWithFlags(ctypes.byref(self._ev), self.DISABLE_SYSTEM_FENCE),
+                    "hipEventCreateWithFlags")
+
+    @staticmethod
+    def _check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def record(self, stream):
+        self._check(self._hip.hipEventRecord(self._ev, stream.cuda_stream), "hipEventRecord")
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end` (both recorded and complete)."""
+        import ctypes
+        ms = ctypes.c_float()
+        self._check(self._hip.hipEventElapsedTime(ctypes.byref(ms), self._ev, end._ev), "hipEventElapsedTime")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self._ev:
+            self._hip.hipEventDestroy(self._ev)
+
+
 def timed_events(fn, n, stream, batches=5):
     """Per-launch duration (ms) of fn(): HIP events on `stream` around batches
     of n back-to-back launches (so no event sits between two launches);
@@ -72,7 +116,8 @@ def bench_step(mx, steps, warmup):
     """The MXFP4 step on one stream: W's quantize, A's quantize, the GEMM.
     (Running W's quantize on a second stream beside A's measured no faster.)
     Inside the timed steps only two events per step, around the GEMM on its
-    launch stream; the quantizers' own times come from a separate pass."""
+    launch stream (timing-only events, TimingEvent); the quantizers' own
+    times come from a separate pass."""
     import torch
     from microscaling_block_scaled_amd.synth import make
     d = make("mxfp4_mlp")
@@ -102,7 +147,7 @@ def bench_step(mx, steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    ev = [[TimingEvent() for _ in range(2)] for _ in range(steps)]
     t0 = time.perf_counter()
     for s in range(steps):
         step(ev[s])
