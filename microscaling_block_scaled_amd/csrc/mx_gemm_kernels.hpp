@@ -398,7 +398,8 @@ static hipError_t gemm_i8_launch(const void* aq, const uint8_t* as, const void* 
 // K offset hit distinct LDS banks.  The E8M0 scales travel separately, 32
 // bytes (1024 elements of K) per row at a time, into two alternating LDS
 // buffers: one 16-byte load per lane pair and row instead of a few bytes per
-// row and stage.  Every offset that can reach past a matrix (rows past M or N,
+// row and stage, the loads of a chunk either with its first stage or (SPREAD)
+// one per stage over the stages before it.  Every offset that can reach past a matrix (rows past M or N,
 // the last scale chunk of a row) is in the range-checked VGPR offset of its
 // load, relative to a buffer resource that starts at the tile.
 //
