@@ -127,6 +127,32 @@ def test_whole_tile_shapes(mx, oracle, fmt):
     run_both(mx, oracle, x32, fmt, 2, 1, seed=4, off=2, what="whole fp32 tiles col sr")
 
 
+@pytest.mark.parametrize("fmt", range(6))
+def test_dual_xcd_tile_blocks(mx, oracle, fmt):
+    """Fused row + column output on tile grids that split into 8 x 8 tile
+    blocks per XCD (a multiple of 512 tiles of 128 rows x 256 source bytes),
+    whole and with ragged last tiles and partial blocks, bf16 and fp32, RNE
+    and SR with the transform; outputs inside guard bands."""
+    from microscaling_block_scaled_amd.synth import make
+    rng = np.random.default_rng(70 + fmt)
+    x32 = (rng.standard_t(3, (1024, 4096)) * np.exp2(rng.uniform(-20, 20, (1024, 1)))).astype(np.float32)
+    cases = [(make("quant_sweep", {"X": (2048, 4096)}, seed=12)["X"], 0, "bf16 2048x4096"),
+             (make("quant_sweep", {"X": (2045, 4056)}, seed=13)["X"], 0, "bf16 2045x4056 ragged"),
+             (x32, 0, "fp32 1024x4096"),
+             (make("quant_sweep", {"X": (2048, 4096)}, seed=14)["X"], 1, "bf16 2048x4096 h32 sr")]
+    for x, sr, what in cases:
+        rows, cols = x.shape
+        say("quantize dual blocks", what, FMT_NAMES[fmt])
+        g = guarded_quant_out(mx, fmt, rows, cols, 3)
+        got = mx.quantize(dev(x), fmt, 3, sr, bool(sr), 0x0F0F1234 if sr else 0, 77 if sr else 0, 3 if sr else 0,
+                          out={k: v.t for k, v in g.items()})
+        torch.cuda.synchronize()
+        check_guards(g, what)
+        want = oracle.quantize(x, fmt, 3, sr, oracle.FLAG_HADAMARD32 if sr else 0, 77 if sr else 0,
+                               3 if sr else 0, 0x0F0F1234 if sr else 0)
+        assert_same_bits(got, want, what)
+
+
 @pytest.mark.parametrize("fmt", [4, 0, 2])
 def test_hadamard_and_sr(mx, oracle, fmt):
     """The FP4 recipe: Hadamard-32 on every block, SR (seed 42) on A, RNE on W;
