@@ -698,97 +698,101 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SR && SRC =
   const int tc_eff = (int)(p.cols_x - c0 < T::TC ? p.cols_x - c0 : T::TC);
   const int tr_pad = (int)(p.rows - r0 < T::TR ? p.rows - r0 : T::TR);
   const int tc_pad = (int)(p.cols - c0 < T::TC ? p.cols - c0 : T::TC);
-  const bool whole = tr_eff == T::TR && tc_eff == T::TC;
+  const bool whole_tile = tr_eff == T::TR && tc_eff == T::TC;
   // whole bf16 tiles with rows of s_row in whole dwords: the row-wise scales
   // are gathered in LDS and written one dword per row
   constexpr bool FAST = SRC == SRC_BF16 && !HAD && HwPath<F, SR>::value;
   constexpr bool FASTCOL = SRC == SRC_BF16 && !HAD && HwPath32<F, SR>::value;
-  const bool gather = FAST && ROWS && whole && (p.cols & 127) == 0;
-  const int cq = tid % T::CPRW, sub = tid / T::CPRW;
-  const HadLane hl = had_lane(p.signs, cq & 3);  // tile columns start at a multiple of 4 chunks
-  // chunk cq (8 elements) takes part when it lies in a block of the padded
-  // tile; `valid` of its elements exist
-  const bool col_ok = cq * 8 < tc_pad;
-  const int valid = tc_eff - cq * 8;
+  // The tile's work, compiled twice: for whole tiles (WH: straight-line
+  // 16-byte loads, so the compiler counts them exactly and the first passes
+  // can start before the last loads land) and for ragged ones.
+  auto body = [&](auto WH_) {
+    constexpr bool WH = decltype(WH_)::value;
+    constexpr bool whole = WH;
+    const bool gather = FAST && ROWS && whole && (p.cols & 127) == 0;
+    const int cq = tid % T::CPRW, sub = tid / T::CPRW;
+    const HadLane hl = had_lane(p.signs, cq & 3);  // tile columns start at a multiple of 4 chunks
+    // chunk cq (8 elements) takes part when it lies in a block of the padded
+    // tile; `valid` of its elements exist
+    const bool col_ok = cq * 8 < tc_pad;
+    const int valid = tc_eff - cq * 8;
 
-  uint32_t raw[T::PASSES][T::RAWN];
+    uint32_t raw[T::PASSES][T::RAWN];
+    if constexpr (WH) {
+      // every chunk exists: whole 16-byte loads, in pass order
 #pragma unroll
-  for (int pp = 0; pp < T::PASSES; pp++) {
-    const int row = pp * T::RPP + sub;
-    if (row < tr_pad && col_ok) {
-      if (row < tr_eff && valid > 0) {
-        const uint8_t* src = p.x + (r0 + row) * p.ld_bytes + (c0 + 8 * cq) * T::ESZ;
-        load_elems<T::ESZ, 8, true>(src, valid, raw[pp]);
-      } else {
+      for (int pp = 0; pp < T::PASSES; pp++) {
+        const uint8_t* src = p.x + (r0 + pp * T::RPP + sub) * p.ld_bytes + (c0 + 8 * cq) * T::ESZ;
 #pragma unroll
-        for (int k = 0; k < T::RAWN; k++) raw[pp][k] = 0u;
-      }
-    }
-  }
-  // All of the tile is needed before the first stores go out.  Waiting for
-  // the loads here, explicitly, tells the compiler they are complete, so it
-  // does not wait again (for the stores then in flight) before each pass.
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-#pragma unroll
-  for (int pp = 0; pp < T::PASSES; pp++) {
-    const int row = pp * T::RPP + sub;
-    if (row < tr_pad && col_ok) {
-      uint32_t v[8];
-      widen8<SRC>(raw[pp], v);
-      if (ROWS && row < tr_eff) {
-        if constexpr (FAST) {
-          row_chunk_bf16<F>(p, r0 + row, (c0 >> 3) + cq, raw[pp],
-                            gather ? (uint8_t*)sc_lds + 4 * row + (cq >> 2) : nullptr);
-        } else {
-          uint32_t w[8];
-#pragma unroll
-          for (int k = 0; k < 8; k++) w[k] = v[k];
-          row_chunk<F, SR, HAD>(p, r0 + row, (c0 >> 3) + cq, w, hl);
+        for (int j = 0; j < T::RAWN / 4; j++) {
+          const uint4 t = ld_stream(src + 16 * j);
+          raw[pp][4 * j] = t.x; raw[pp][4 * j + 1] = t.y; raw[pp][4 * j + 2] = t.z; raw[pp][4 * j + 3] = t.w;
         }
       }
-      const int sw = whole ? tile_swz(row) : 0;
-      uint8_t* dst = lds + row * T::ROWB;
-      if constexpr (SRC == SRC_BF16) {
-        *(uint4*)(dst + 16 * (cq ^ sw)) = make_uint4(raw[pp][0], raw[pp][1], raw[pp][2], raw[pp][3]);
-      } else {
-        *(uint4*)(dst + 16 * ((2 * cq) ^ sw)) = make_uint4(v[0], v[1], v[2], v[3]);
-        *(uint4*)(dst + 16 * ((2 * cq + 1) ^ sw)) = make_uint4(v[4], v[5], v[6], v[7]);
-      }
-    }
-  }
-  __syncthreads();
-
-  if (gather && tid < T::TR)
-    *(uint32_t*)(p.s_row + (r0 + tid) * (p.cols >> 5) + (c0 >> 5)) = sc_lds[tid];
-  if (whole) {
-    const int lane = tid & 63, qb = lane & 3;
-    const int d = 16 * (tid >> 6) + (lane >> 2);
-    const uint8_t* src = lds + 32 * qb * T::ROWB + 16 * ((d >> 2) ^ (4 * qb)) + 4 * (d & 3);
-    uint32_t w[32];
-#pragma unroll
-    for (int i = 0; i < 32; i++) w[i] = *(const uint32_t*)(src + i * T::ROWB);
-    if constexpr (FASTCOL) {
-      col_pair_bf16<F>(p, w, c0 + 2 * d, r0, qb);
-    } else if constexpr (SR && SRC == SRC_BF16) {
-      col_pair_sr<F, HAD, true>(p, w, c0 + 2 * d, r0, qb);
+      // the first half of the passes goes ahead while the second half's
+      // loads are in flight
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (T::RAWN / 4) * (T::PASSES / 2));
     } else {
 #pragma unroll
-      for (int k = 0; k < T::CPT; k++) {
-        uint32_t v[32];
+      for (int pp = 0; pp < T::PASSES; pp++) {
+        const int row = pp * T::RPP + sub;
+        if (row < tr_pad && col_ok) {
+          if (row < tr_eff && valid > 0) {
+            const uint8_t* src = p.x + (r0 + row) * p.ld_bytes + (c0 + 8 * cq) * T::ESZ;
+            load_elems<T::ESZ, 8, true>(src, valid, raw[pp]);
+          } else {
 #pragma unroll
-        for (int i = 0; i < 32; i++)
-          v[i] = SRC == SRC_BF16 ? (k == 0 ? w[i] << 16 : w[i] & 0xFFFF0000u) : w[i];
-        col_quad<F, SR, HAD>(p, v, c0 + T::CPT * d + k, r0, qb);
+            for (int k = 0; k < T::RAWN; k++) raw[pp][k] = 0u;
+          }
+        }
+      }
+      // All of the tile is needed before the first stores go out.  Waiting for
+      // the loads here, explicitly, tells the compiler they are complete, so it
+      // does not wait again (for the stores then in flight) before each pass.
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    }
+#pragma unroll
+    for (int pp = 0; pp < T::PASSES; pp++) {
+      const int row = pp * T::RPP + sub;
+      if (WH || (row < tr_pad && col_ok)) {
+        uint32_t v[8];
+        widen8<SRC>(raw[pp], v);
+        if (ROWS && (WH || row < tr_eff)) {
+          if constexpr (FAST) {
+            row_chunk_bf16<F>(p, r0 + row, (c0 >> 3) + cq, raw[pp],
+                              gather ? (uint8_t*)sc_lds + 4 * row + (cq >> 2) : nullptr);
+          } else {
+            uint32_t w[8];
+#pragma unroll
+            for (int k = 0; k < 8; k++) w[k] = v[k];
+            row_chunk<F, SR, HAD>(p, r0 + row, (c0 >> 3) + cq, w, hl);
+          }
+        }
+        const int sw = whole ? tile_swz(row) : 0;
+        uint8_t* dst = lds + row * T::ROWB;
+        if constexpr (SRC == SRC_BF16) {
+          *(uint4*)(dst + 16 * (cq ^ sw)) = make_uint4(raw[pp][0], raw[pp][1], raw[pp][2], raw[pp][3]);
+        } else {
+          *(uint4*)(dst + 16 * ((2 * cq) ^ sw)) = make_uint4(v[0], v[1], v[2], v[3]);
+          *(uint4*)(dst + 16 * ((2 * cq + 1) ^ sw)) = make_uint4(v[4], v[5], v[6], v[7]);
+        }
       }
     }
-  } else {
-    const int qb = tid >> 6, g = tid & 63;
-    if (32 * qb < tr_eff && g * T::CPT < tc_eff) {
+    __syncthreads();
+
+    if (gather && tid < T::TR)
+      *(uint32_t*)(p.s_row + (r0 + tid) * (p.cols >> 5) + (c0 >> 5)) = sc_lds[tid];
+    if (whole) {
+      const int lane = tid & 63, qb = lane & 3;
+      const int d = 16 * (tid >> 6) + (lane >> 2);
+      const uint8_t* src = lds + 32 * qb * T::ROWB + 16 * ((d >> 2) ^ (4 * qb)) + 4 * (d & 3);
       uint32_t w[32];
 #pragma unroll
-      for (int i = 0; i < 32; i++) w[i] = *(const uint32_t*)(lds + (32 * qb + i) * T::ROWB + g * 4);
-      if constexpr (SR && SRC == SRC_BF16) {
-        col_pair_sr<F, HAD, false>(p, w, c0 + 2 * g, r0, qb);
+      for (int i = 0; i < 32; i++) w[i] = *(const uint32_t*)(src + i * T::ROWB);
+      if constexpr (FASTCOL) {
+        col_pair_bf16<F>(p, w, c0 + 2 * d, r0, qb);
+      } else if constexpr (SR && SRC == SRC_BF16) {
+        col_pair_sr<F, HAD, true>(p, w, c0 + 2 * d, r0, qb);
       } else {
 #pragma unroll
         for (int k = 0; k < T::CPT; k++) {
@@ -796,11 +800,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SR && SRC =
 #pragma unroll
           for (int i = 0; i < 32; i++)
             v[i] = SRC == SRC_BF16 ? (k == 0 ? w[i] << 16 : w[i] & 0xFFFF0000u) : w[i];
-          if (c0 + g * T::CPT + k < p.cols_x) col_block<F, SR, HAD>(p, v, c0 + g * T::CPT + k, r0 + 32 * qb);
+          col_quad<F, SR, HAD>(p, v, c0 + T::CPT * d + k, r0, qb);
+        }
+      }
+    } else {
+      const int qb = tid >> 6, g = tid & 63;
+      if (32 * qb < tr_eff && g * T::CPT < tc_eff) {
+        uint32_t w[32];
+#pragma unroll
+        for (int i = 0; i < 32; i++) w[i] = *(const uint32_t*)(lds + (32 * qb + i) * T::ROWB + g * 4);
+        if constexpr (SR && SRC == SRC_BF16) {
+          col_pair_sr<F, HAD, false>(p, w, c0 + 2 * g, r0, qb);
+        } else {
+#pragma unroll
+          for (int k = 0; k < T::CPT; k++) {
+            uint32_t v[32];
+#pragma unroll
+            for (int i = 0; i < 32; i++)
+              v[i] = SRC == SRC_BF16 ? (k == 0 ? w[i] << 16 : w[i] & 0xFFFF0000u) : w[i];
+            if (c0 + g * T::CPT + k < p.cols_x) col_block<F, SR, HAD>(p, v, c0 + g * T::CPT + k, r0 + 32 * qb);
+          }
         }
       }
     }
-  }
+  };
+  if (whole_tile) body(std::true_type{});
+  else body(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------
