@@ -6,6 +6,8 @@
 // and the GEMM's MX-output epilogue.
 #pragma once
 
+#include <type_traits>
+
 #include "mx_device.hpp"
 
 namespace mx {
@@ -237,6 +239,48 @@ __device__ __forceinline__ uint32_t sr_fp4_hw8(const uint32_t v[8], uint32_t cod
   return __builtin_amdgcn_perm(b1, b0, 0x0C0C0400u) | __builtin_amdgcn_perm(b3, b2, 0x04000C0Cu);
 }
 
+// FP8 (E4M3, E5M2) codes of 8 elements with stochastic rounding through
+// gfx950's SR conversion, one element per instruction with the seed ~r.
+// Measured against the definition (4M random elements and scale codes, and as
+// many again with r agreeing with the discarded fraction in its top 16 to 32
+// bits): where the result is normal (|V / X| >= 2^emin) the discarded fraction
+// has at most 21 bits and the instruction rounds up exactly when r < F, and it
+// saturates like the RNE conversion once fix_sat is applied; where the result
+// is subnormal it compares fewer bits than the definition.  So `redo` is set
+// for a group holding a nonzero element below 2^emin * X (fp32-subnormal
+// inputs included, which the exact conversion flushes), and such a group takes
+// the exact conversion.  Needs code + emin >= 1 (the bound is a normal fp32).
+template <int F>
+__device__ __forceinline__ Pack8 sr_fp8_hw8(const uint32_t v[8], uint32_t code, const uint32_t rnd[8],
+                                            bool& redo) {
+  const float S = __builtin_bit_cast(float, code << 23);        // 2^(code - 127)
+  const uint32_t lim = ((code + Fmt<F>::emin) << 23) - 1u;  // bits of 2^emin * X, less one
+  auto cvt = [&](uint32_t old, int k, auto B) {
+    constexpr int b = decltype(B)::value;
+    const float f = __builtin_bit_cast(float, v[k]);
+    if constexpr (F == E4M3) return (uint32_t)__builtin_amdgcn_cvt_scalef32_sr_fp8_f32(old, f, ~rnd[k], S, b);
+    else return (uint32_t)__builtin_amdgcn_cvt_scalef32_sr_bf8_f32(old, f, ~rnd[k], S, b);
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
+  using B3 = std::integral_constant<int, 3>;
+  Pack8 o;
+  bool bad = false;
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    uint32_t w = cvt(0u, 4 * h, B0{});
+    w = cvt(w, 4 * h + 1, B1{});
+    w = cvt(w, 4 * h + 2, B2{});
+    w = cvt(w, 4 * h + 3, B3{});
+    o.w[h] = fix_sat<F>(w);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; k++) bad |= ((v[k] & 0x7FFFFFFFu) - 1u) < lim;
+  redo = bad;
+  return o;
+}
+
 // Codes of 8 elements of a block with scale `code`.  `v` holds fp32 bits;
 // `rnd` the stochastic-rounding words (ignored for RNE).
 template <int F, bool SR>
@@ -251,6 +295,11 @@ __device__ __forceinline__ Pack8 convert8(const uint32_t v[8], uint32_t code, co
   if (!SR && (F == E4M3 || F == E5M2 || F == E2M1) && code >= (uint32_t)DazFree<F>::value)
     return hw_convert8<F>(v, code);
   if (!SR && F == INT8 && code >= (uint32_t)DazFree<F>::value) return int8_convert8(v, code);
+  if (SR && (F == E4M3 || F == E5M2) && code >= (uint32_t)(1 - Fmt<F>::emin)) {  // 0xFF returned above
+    bool redo;
+    const Pack8 o = sr_fp8_hw8<F>(v, code, rnd, redo);
+    if (!redo) return o;
+  }
   if (SR && F == E2M1 && code >= 24u) {  // code 0xFF returned above
     bool redo;
     Pack8 o;

@@ -183,6 +183,57 @@ def test_sr_fraction_ties_with_random_word(mx, oracle, col_blocks):
     run_both(mx, oracle, x, 4, lay, 1, seed=seed, off=off, what="sr ties")
 
 
+FP8_SR = {0: (3, -6, 448.0), 1: (2, -14, 57344.0)}  # E4M3, E5M2: mantissa bits, emin, max-normal
+
+
+def fp8_sr_aimed_tensor(oracle, fmt, rows, cols, col_blocks, seed, off):
+    """fp32 [rows, cols] of FP8 blocks whose first element is max-normal * 2^s
+    (block scale 2^s) and whose other elements have a discarded fraction aimed
+    at their own SR word: for normal results (|V / X| >= 2^emin) the fraction's
+    23 - mbits bits equal the word's top bits, plus -1, 0 or +1; for subnormal
+    results the fraction's top 24 bits equal the word's top 24, plus -1, 0 or
+    +1 in the last bit, at depths of 0 to 8 binades below the smallest normal."""
+    mb, emin, maxn = FP8_SR[fmt]
+    D = 23 - mb
+    rng = np.random.default_rng(31 + fmt)
+    x = np.zeros((rows, cols), np.float32)
+    lay_id = 1 if col_blocks else 0
+    for r in range(rows):
+        for c in range(cols):
+            k, blk, line = (r % 32, r // 32, c) if col_blocks else (c % 32, c // 32, r)
+            scale = 2.0 ** ((blk * 5 + line * 3) % 30 - 15)
+            sign = -1.0 if rng.integers(0, 2) else 1.0
+            if k == 0:
+                x[r, c] = sign * maxn * scale
+                continue
+            w = oracle.sr_word(seed, off, lay_id, r * cols + c)
+            delta = int(rng.integers(-1, 2))
+            if rng.integers(0, 2):  # normal result in a random binade
+                e = int(rng.integers(emin, emin + 8))
+                n = int(rng.integers(1 << mb, 1 << (mb + 1)))
+                f = min(max((w >> (32 - D)) + delta, 0), (1 << D) - 1)
+                y = (n + f * 2.0 ** -D) * 2.0 ** (e - mb)
+            else:  # subnormal result: below one grid step of the subnormals, deep or not
+                depth = int(rng.integers(0, 9))
+                f = min(max((w >> 8) + delta, 1), (1 << 24) - 1)
+                y = f * 2.0 ** -24 * 2.0 ** (emin - mb - depth)
+            x[r, c] = np.float32(sign * y * scale)
+    return x
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("col_blocks", [False, True])
+def test_fp8_sr_aimed_words(mx, oracle, fmt, col_blocks):
+    """FP8 stochastic rounding with each element's random word aimed at its
+    discarded fraction (the decision then rests on the word's last bits), in
+    the normal range the hardware conversion decides and in the subnormal
+    range where the kernels redo it exactly: bit-exact with the oracle."""
+    rows, cols = (256, 64) if col_blocks else (64, 256)
+    seed, off = 0xF8F8, 5
+    x = fp8_sr_aimed_tensor(oracle, fmt, rows, cols, col_blocks, seed, off)
+    run_both(mx, oracle, x, fmt, 2 if col_blocks else 1, 1, seed=seed, off=off, what="fp8 sr aimed")
+
+
 def test_special_blocks(mx, oracle):
     """Zero, subnormal, Inf / NaN, fp32-max and fp32-min-normal blocks."""
     x = np.zeros((64, 256), np.float32)
