@@ -323,6 +323,16 @@ def test_full_size_fp4_recipe(mx, oracle):
     run_both(mx, oracle, d["A"], 4, 1, 1, True, 0, 42, 0, what="A 8192x14336 h32 sr")
 
 
+def test_full_size_fp8_sr_gradient(mx, oracle):
+    """The gradient-like bf16 A [4096 x 14336] ~ N(0, 1e-3) of the MXFP8
+    grad shape with stochastic rounding, as the linear layer's backward
+    quantizes a gradient: E5M2 row-wise, E4M3 column-wise with the transform."""
+    from microscaling_block_scaled_amd.synth import make
+    a = make("mxfp8_grad")["A"]
+    run_both(mx, oracle, a, 1, 1, 1, False, 0, 42, 0, what="grad 4096x14336 e5m2 row sr")
+    run_both(mx, oracle, a, 0, 2, 1, True, 0, 42, 0, what="grad 4096x14336 e4m3 col-T h32 sr")
+
+
 @pytest.mark.parametrize("fmt", range(6))
 def test_strided_source_and_guards(mx, oracle, fmt):
     """The source is a column slice of a wider tensor (ld_x > cols, the slice
