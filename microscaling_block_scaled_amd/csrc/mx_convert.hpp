@@ -266,7 +266,6 @@ __device__ __forceinline__ Pack8 sr_fp8_hw8(const uint32_t v[8], uint32_t code, 
   using B2 = std::integral_constant<int, 2>;
   using B3 = std::integral_constant<int, 3>;
   Pack8 o;
-  bool bad = false;
 #pragma unroll
   for (int h = 0; h < 2; h++) {
     uint32_t w = cvt(0u, 4 * h, B0{});
@@ -275,9 +274,12 @@ __device__ __forceinline__ Pack8 sr_fp8_hw8(const uint32_t v[8], uint32_t code, 
     w = cvt(w, 4 * h + 3, B3{});
     o.w[h] = fix_sat<F>(w);
   }
+  // 2|V| - 2 (the sign shifted out, zeros wrapping to the top), least over
+  // the group, against 2 (bound - 1): one shift-add per element, one compare
+  uint32_t m = 0xFFFFFFFFu;
 #pragma unroll
-  for (int k = 0; k < 8; k++) bad |= ((v[k] & 0x7FFFFFFFu) - 1u) < lim;
-  redo = bad;
+  for (int k = 0; k < 8; k++) m = umin(m, (v[k] << 1) - 2u);
+  redo = m < 2u * lim;
   return o;
 }
 

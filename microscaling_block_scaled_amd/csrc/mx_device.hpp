@@ -192,6 +192,7 @@ __device__ __forceinline__ float quad_xor2f(float v) {
 }
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
 
 // fp32 value of 1/sqrt(32) rounded to nearest (0x3E3504F3).
 __device__ __forceinline__ float inv_sqrt32() { return __builtin_bit_cast(float, 0x3E3504F3u); }
