@@ -172,8 +172,10 @@ def bench_step(mx, steps, warmup):
             "sample": sample}
 
 
-def bench_quant(mx, name, x_host, fmt, layouts, rounds=100):
-    """Median kernel time of one quantize over rotating buffer sets (>= 1 GiB)."""
+def bench_quant(mx, name, x_host, fmt, layouts, rounds=100, rnd=0, had=False, seed=0):
+    """Median kernel time of one quantize over rotating buffer sets (>= 1 GiB);
+    `rnd`, `had`, `seed`: stochastic rounding, the Hadamard-32 transform and
+    the Philox key."""
     import torch
     rows, cols = x_host.shape
     in_bytes = x_host.nbytes
@@ -186,10 +188,11 @@ def bench_quant(mx, name, x_host, fmt, layouts, rounds=100):
     nsets = max(2, int((1 << 30) // (in_bytes + out_bytes)) + 1)
     x0 = dev_bf16(x_host)
     xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
-    outs = [mx.quantize(x, fmt, layouts) for x in xs]
+    outs = [mx.quantize(x, fmt, layouts, rnd, had, 0, seed, 0) for x in xs]
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
-    med, avg = timed_events(lambda i: mx.quantize(xs[i % nsets], fmt, layouts, out=outs[i % nsets]),
+    med, avg = timed_events(lambda i: mx.quantize(xs[i % nsets], fmt, layouts, rnd, had, 0, seed, 0,
+                                                  out=outs[i % nsets]),
                             max(rounds // 5, 4), st)
     gbs = (in_bytes + out_bytes) / (med * 1e-3) / 1e9
     del xs, outs
@@ -446,6 +449,17 @@ def main():
         del x
         # memory-only floors of the same sizes: a copy of the sweep's bf16 input and of the
         # dual-layout one
+        # a gradient's quantizes in the linear layer's backward: stochastic rounding to FP8
+        # (row-wise, and column-wise with the transform), on the grad-like A of the MXFP8
+        # grad shape
+        x = make("mxfp8_grad")["A"]
+        for fname, f in (("e4m3", mx.E4M3), ("e5m2", mx.E5M2)):
+            ks[f"sr_grad_{fname}_row"] = bench_quant(
+                mx, f"bf16 [4096x14336] N(0,1e-3) -> {fname} row, SR", x, f, 1, rnd=mx.SR, seed=42)
+            ks[f"sr_grad_{fname}_colt_h32"] = bench_quant(
+                mx, f"bf16 [4096x14336] N(0,1e-3) -> {fname} col-T, H32 + SR", x, f, 2, rnd=mx.SR,
+                had=True, seed=42)
+        del x
         ks["copy_floor_4096x4096_bf16"] = bench_copy("device copy of 32 MiB (the sweep input)",
                                                      4096 * 4096 * 2)
         ks["copy_floor_16384x4096_bf16"] = bench_copy("device copy of 128 MiB (the dual-layout input)",
